@@ -1,0 +1,416 @@
+"""Protocol oracle: models of the seq/parity/flag protocol and of the signal-pad
+barrier (test infrastructure only; only tests/, the smoke check and the
+benchmark's CPU-baseline leg may import it).
+
+Three models, each written from the pages' description, none sharing code
+with the HIP library:
+
+``sequential_model``
+    One rank (this GPU) whose W-1 peers are virtual: their partials already
+    sit in recv slots and a host proxy posts their flags. Runs K calls one
+    after the other and predicts every output and the final state of every
+    protocol word (page "arx.cu": protocol comment steps 1-3, arx_kernel).
+
+``check_protocol``
+    Brute-force exploration of every interleaving of a symmetric W-rank
+    system (page "arx.cu"): per rank, G workgroups run the copy, arrival
+    count, publish, flag wait (workgroup 0), go broadcast, reduction and
+    last-block-out steps of arx_kernel, and a proxy posts, for every
+    published seq in order, the partial into each peer's recv slot and then
+    the flag. Checks that every reduction reads exactly the data of its own
+    seq from every rank, that no reachable state is stuck before all calls
+    finish, that both counters are zero whenever a kernel ends, and that a
+    peer's flag never runs more than one seq ahead of this rank's publish.
+    Mutants switch off one safety rule each; each must fail.
+
+``check_barrier``
+    Brute-force exploration of the blockwise signal-pad barrier (page
+    "triton_barrier.py", send_signal / wait_signal / blockwise_barrier): W
+    ranks, lane s of rank r CASes 0->1 on slot r of rank s's pad and then
+    CASes 1->0 on slot s of its own pad, for K consecutive rounds on one block
+    id. Checks that no rank leaves a round before every rank entered it, that
+    nothing deadlocks, and that every pad is all zero whenever no barrier is
+    in flight. Mutants B1 and B2 must fail.
+
+The brute-force models are sequentially consistent: they check the protocol's
+logic, not the memory ordering of any particular GPU.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import reduce as _reduce
+
+U32 = 0xFFFFFFFF
+
+# --------------------------------------------------------------------------
+# Sequential single-GPU model with virtual peers
+# --------------------------------------------------------------------------
+
+LOCKSTEP = "lockstep"   # peers post seq s once this rank has published s
+RUNAHEAD = "runahead"   # peers post seq s once this rank has published s - 1
+MANUAL = "manual"       # flags are posted by the caller
+
+
+@dataclass
+class ProtocolState:
+    """Every protocol word of one rank (page "arx.cu": struct Ctl, struct Dev)."""
+    W: int
+    rank: int
+    seq_dev: int = 0            # device u32: last completed seq
+    cnt: List[int] = field(default_factory=lambda: [0, 0])  # arrival / finish counters
+    go: int = 0                 # device u32: seq whose peer data has all arrived
+    ctl_seq: int = 0            # pinned u64: last published seq
+    ctl_bytes: List[int] = field(default_factory=lambda: [0, 0])  # bytes per parity
+    ctl_done: int = 0           # pinned u64: last seq summed
+    flags: List[int] = None     # pinned u64 per source rank (own entry unused)
+    posted: int = 0             # last seq the proxy posted
+    send: List[np.ndarray] = None  # send slot per parity
+
+    def __post_init__(self):
+        if self.flags is None:
+            self.flags = [0] * self.W
+
+
+def _post(st: ProtocolState, s: int) -> None:
+    """The virtual peers publish seq s: every flag but this rank's becomes s.
+    Seqs are posted in order, none skipped (page "arx.cu", protocol comment
+    on the proxy posting every seq in order)."""
+    if s != st.posted + 1:
+        raise ValueError(f"seq {s} posted out of order after {st.posted}")
+    for src in range(st.W):
+        if src != st.rank:
+            st.flags[src] = s
+    st.posted = s
+
+
+def sequential_model(calls: Sequence[Tuple[np.ndarray, int]], recv, W: int, rank: int = 0,
+                     max_n: Optional[int] = None, mode: str = LOCKSTEP,
+                     state: Optional[ProtocolState] = None):
+    """Runs the calls (each ``(in_bits, n)``) through the one-shot path in order.
+
+    recv[par][src] holds peer src's partial for parity par. Returns
+    ``(state, outs)`` where outs[k] holds the first n elements of call k's
+    output. In MANUAL mode no flags are posted, so a call whose flags are
+    missing raises (the GPU would wait for them).
+    """
+    if max_n is None:
+        max_n = max((n for _, n in calls), default=0)
+    st = state or ProtocolState(W=W, rank=rank)
+    if st.send is None:
+        st.send = [np.zeros(max_n, np.uint16), np.zeros(max_n, np.uint16)]
+    if mode == RUNAHEAD and st.posted == 0:
+        _post(st, 1)                       # seq 1 needs only seq 0, published at init
+    outs = []
+    for x, n in calls:
+        seq = (st.seq_dev + 1) & U32       # seq_dev is a device u32
+        par = seq & 1
+        st.send[par][:n] = np.asarray(x, dtype=np.uint16)[:n]       # copy into the send slot
+        st.ctl_bytes[par] = 2 * n
+        st.ctl_seq = seq                   # last arriver publishes
+        if mode == LOCKSTEP:
+            _post(st, seq)
+        elif mode == RUNAHEAD:
+            _post(st, seq + 1)
+        if any(st.flags[src] < seq for src in range(W) if src != rank):
+            raise RuntimeError(f"seq {seq}: a peer flag never reached seq (flags {st.flags})")
+        st.go = seq                        # workgroup 0 releases the others
+        parts = [st.send[par] if src == rank else recv[par][src] for src in range(W)]
+        outs.append(_reduce.reduce(parts, n=n))
+        st.seq_dev = seq                   # last block out
+        st.ctl_done = seq
+    return st, outs
+
+
+# --------------------------------------------------------------------------
+# Brute-force interleavings of the symmetric W-rank protocol
+# --------------------------------------------------------------------------
+
+# Workgroup program counters, in program order.
+READSEQ, COPY, ARRIVE, WAIT, REDUCE, LASTOUT, DONE, FIN = range(8)
+
+MUTANTS = {
+    None: "the protocol as the page states it",
+    "M1": "proxy posts only the latest published seq, skipping the ones between",
+    "M2": "one send/recv buffer (parity always 0)",
+    "M3": "proxy writes the flag before the data",
+    "M4": "one counter shared by the arrival and the finish phase",
+    "M5": "workgroups other than 0 do not wait for go",
+}
+
+
+def _tag(src: int, s: int) -> int:
+    return src * 64 + s   # 0 = never written
+
+
+@dataclass
+class CheckResult:
+    ok: bool
+    states: int
+    violation: Optional[str] = None
+    finals: int = 0
+
+
+def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
+                   max_states: int = 5_000_000) -> CheckResult:
+    """Explores every interleaving of W ranks x G workgroups x S calls.
+
+    Rank state tuple: (c, pcs, ss, cnt0, cnt1, go, seq_dev, ctl_seq, done,
+    send, recv, flag, posted, pcur, ppos) where c is the running call (S + 1
+    after the last), pcs/ss the per-workgroup program counter and seq,
+    send[par*G+g] / recv[(par*W+src)*G+g] data tags, flag[src] the flags this
+    rank received, and (posted, pcur, ppos) the proxy's last posted seq, the
+    seq it is posting (0 when idle) and its position in that post's actions.
+    """
+    if mutant not in MUTANTS:
+        raise ValueError(mutant)
+    nbuf = 1 if mutant == "M2" else 2
+
+    def par_of(s):
+        return 0 if mutant == "M2" else s & 1
+
+    # Proxy actions for one seq, staggered peer order r+1, r+2, ... (page
+    # "arx.cu": each rank sends to the next ranks in turn). Data first, then
+    # the flag on the same ordered channel; M3 swaps them.
+    def actions(r):
+        acts = []
+        for step in range(1, W):
+            j = (r + step) % W
+            data = [("data", j, g) for g in range(G)]
+            flag = [("flag", j, 0)]
+            acts += (flag + data) if mutant == "M3" else (data + flag)
+        return acts
+
+    acts = [actions(r) for r in range(W)]
+
+    init_rank = (1, (READSEQ,) * G, (0,) * G, 0, 0, 0, 0, 0, 0,
+                 (0,) * (2 * G), (0,) * (2 * W * G), (0,) * W, 0, 0, 0)
+    init = tuple(init_rank for _ in range(W))
+
+    seen = {init}
+    stack = [init]
+    finals = 0
+
+    def replace(state, r, rs):
+        return state[:r] + (rs,) + state[r + 1:]
+
+    while stack:
+        st = stack.pop()
+        succ = []
+        for r in range(W):
+            (c, pcs, ss, cnt0, cnt1, go, seq_dev, ctl_seq, done,
+             send, recv, flag, posted, pcur, ppos) = st[r]
+            # ---- GPU workgroups of rank r
+            if c <= S:
+                for g in range(G):
+                    pc = pcs[g]
+                    s = ss[g]
+                    ns = None
+                    if pc == READSEQ:
+                        s2 = seq_dev + 1
+                        ns = (c, pcs[:g] + (COPY,) + pcs[g + 1:], ss[:g] + (s2,) + ss[g + 1:],
+                              cnt0, cnt1, go, seq_dev, ctl_seq, done, send, recv, flag, posted, pcur, ppos)
+                    elif pc == COPY:
+                        i = par_of(s) * G + g
+                        send2 = send[:i] + (_tag(r, s),) + send[i + 1:]
+                        ns = (c, pcs[:g] + (ARRIVE,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
+                              ctl_seq, done, send2, recv, flag, posted, pcur, ppos)
+                    elif pc == ARRIVE:
+                        old = cnt0
+                        n0 = cnt0 + 1
+                        cs = ctl_seq
+                        if old == G - 1:      # last block publishes and resets
+                            n0 = 0
+                            cs = s
+                        if mutant == "M4":    # one counter for both phases
+                            ns = (c, pcs[:g] + (WAIT,) + pcs[g + 1:], ss, n0, n0, go, seq_dev, cs,
+                                  done, send, recv, flag, posted, pcur, ppos)
+                        else:
+                            ns = (c, pcs[:g] + (WAIT,) + pcs[g + 1:], ss, n0, cnt1, go, seq_dev, cs,
+                                  done, send, recv, flag, posted, pcur, ppos)
+                    elif pc == WAIT:
+                        if g == 0:
+                            if all(flag[j] >= s for j in range(W) if j != r):
+                                ns = (c, pcs[:g] + (REDUCE,) + pcs[g + 1:], ss, cnt0, cnt1, s, seq_dev,
+                                      ctl_seq, done, send, recv, flag, posted, pcur, ppos)
+                        elif mutant == "M5" or go >= s:
+                            ns = (c, pcs[:g] + (REDUCE,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
+                                  ctl_seq, done, send, recv, flag, posted, pcur, ppos)
+                    elif pc == REDUCE:
+                        p = par_of(s)
+                        for j in range(W):
+                            t = send[p * G + g] if j == r else recv[(p * W + j) * G + g]
+                            if t != _tag(j, s):
+                                return CheckResult(False, len(seen), (
+                                    f"rank {r} wg {g} reduced seq {s} with stale data from rank {j} "
+                                    f"(tag {t // 64},{t % 64})"))
+                        ns = (c, pcs[:g] + (LASTOUT,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
+                              ctl_seq, done, send, recv, flag, posted, pcur, ppos)
+                    elif pc == LASTOUT:
+                        base = cnt0 if mutant == "M4" else cnt1
+                        n1 = base + 1
+                        sd, dn = seq_dev, done
+                        if base == G - 1:     # last block out
+                            n1 = 0
+                            sd = s
+                            dn = s
+                        pcs2 = pcs[:g] + (DONE,) + pcs[g + 1:]
+                        c2 = c
+                        if all(x == DONE for x in pcs2):   # the kernel ends
+                            c2 = c + 1
+                            pcs2 = ((READSEQ,) if c2 <= S else (FIN,)) * G
+                            final_cnt = (n1, n1) if mutant == "M4" else (cnt0, n1)
+                            if final_cnt != (0, 0):
+                                return CheckResult(False, len(seen), (
+                                    f"rank {r} kernel {c} ended with counters {final_cnt}"))
+                        if mutant == "M4":
+                            ns = (c2, pcs2, ss, n1, n1, go, sd, ctl_seq, dn, send, recv, flag,
+                                  posted, pcur, ppos)
+                        else:
+                            ns = (c2, pcs2, ss, cnt0, n1, go, sd, ctl_seq, dn, send, recv, flag,
+                                  posted, pcur, ppos)
+                    if ns is not None:
+                        succ.append(replace(st, r, ns))
+            # ---- proxy of rank r
+            if pcur == 0:
+                nxt = None
+                if mutant == "M1":
+                    if ctl_seq > posted:
+                        nxt = ctl_seq
+                elif ctl_seq >= posted + 1:
+                    nxt = posted + 1
+                if nxt is not None:
+                    ns = st[r][:13] + (nxt, 0)
+                    succ.append(replace(st, r, ns))
+            else:
+                kind, j, g = acts[r][ppos]
+                p = par_of(pcur)
+                rj = st[j]
+                if kind == "data":
+                    tag = send[p * G + g]
+                    i = (p * W + r) * G + g
+                    rrecv = rj[10][:i] + (tag,) + rj[10][i + 1:]
+                    rj2 = rj[:10] + (rrecv,) + rj[11:]
+                else:
+                    rflag = rj[11][:r] + (pcur,) + rj[11][r + 1:]
+                    rj2 = rj[:11] + (rflag,) + rj[12:]
+                st2 = replace(st, j, rj2)
+                me = st2[r]
+                if ppos + 1 == len(acts[r]):
+                    me2 = me[:12] + (pcur, 0, 0)
+                else:
+                    me2 = me[:14] + (ppos + 1,)
+                succ.append(replace(st2, r, me2))
+
+        # invariant: a peer's flag at rank r never exceeds r's published seq + 1
+        for r in range(W):
+            ctl_seq = st[r][7]
+            for j in range(W):
+                if j != r and st[r][11][j] > ctl_seq + 1 and mutant is None:
+                    return CheckResult(False, len(seen), (
+                        f"flag from rank {j} at rank {r} is {st[r][11][j]}, more than one "
+                        f"ahead of published {ctl_seq}"))
+
+        if not succ:
+            all_done = all(st[r][0] == S + 1 and st[r][13] == 0 and st[r][12] >= S for r in range(W))
+            if not all_done:
+                desc = "; ".join(f"r{r}: call {st[r][0]} pcs {st[r][1]} seqs {st[r][2]} posted {st[r][12]} "
+                                 f"published {st[r][7]} flags {st[r][11]}" for r in range(W))
+                return CheckResult(False, len(seen), f"deadlock: {desc}")
+            finals += 1
+        for s2 in succ:
+            if s2 not in seen:
+                seen.add(s2)
+                stack.append(s2)
+                if len(seen) > max_states:
+                    raise RuntimeError(f"state space exceeds {max_states}")
+    return CheckResult(True, len(seen), None, finals)
+
+
+# --------------------------------------------------------------------------
+# Brute-force interleavings of the blockwise signal-pad barrier
+# --------------------------------------------------------------------------
+
+SEND, WAITSIG, LANEDONE = range(3)
+
+BARRIER_MUTANTS = {
+    None: "CAS 0->1 to signal, CAS 1->0 to consume (page triton_barrier.py)",
+    "B1": "signal with a plain store of 1 instead of a CAS from 0",
+    "B2": "wait reads the 1 without clearing it",
+}
+
+
+def check_barrier(W: int, K: int, mutant: Optional[str] = None,
+                  max_states: int = 5_000_000) -> CheckResult:
+    """Explores every interleaving of W ranks' lanes over K barrier rounds.
+
+    State: (rounds, lanes, pad). rounds[r] = rounds rank r has entered
+    (1..K, K + 1 once finished); lanes[r*W+s] = lane s's step in rank r's
+    current round; pad[q*W+s] = rank q's pad slot for signals from rank s.
+    A rank starts its next round only when all its lanes finished the current
+    one (the workgroup barrier after blockwise_barrier).
+    """
+    if mutant not in BARRIER_MUTANTS:
+        raise ValueError(mutant)
+    init = ((1,) * W, (SEND,) * (W * W), (0,) * (W * W))
+    seen = {init}
+    stack = [init]
+    finals = 0
+    while stack:
+        st = stack.pop()
+        rounds, lanes, pad = st
+        succ = []
+        for r in range(W):
+            if rounds[r] > K:
+                continue
+            for s in range(W):
+                li = r * W + s
+                step = lanes[li]
+                if step == SEND:
+                    pi = s * W + r          # slot r of rank s's pad
+                    if mutant == "B1" or pad[pi] == 0:
+                        pad2 = pad[:pi] + (1,) + pad[pi + 1:]
+                        succ.append((rounds, lanes[:li] + (WAITSIG,) + lanes[li + 1:], pad2))
+                elif step == WAITSIG:
+                    pi = r * W + s          # slot s of this rank's pad
+                    if pad[pi] == 1:
+                        pad2 = pad if mutant == "B2" else pad[:pi] + (0,) + pad[pi + 1:]
+                        lanes2 = lanes[:li] + (LANEDONE,) + lanes[li + 1:]
+                        succ.append((rounds, lanes2, pad2))
+            if all(lanes[r * W + s] == LANEDONE for s in range(W)):
+                k = rounds[r]
+                # rank r leaves round k: every rank must have entered round k
+                for q in range(W):
+                    if rounds[q] < k:
+                        return CheckResult(False, len(seen), (
+                            f"rank {r} left round {k} before rank {q} entered it"))
+                nxt = (SEND,) if k + 1 <= K else (LANEDONE,)
+                rounds2 = rounds[:r] + (k + 1,) + rounds[r + 1:]
+                lanes2 = lanes[:r * W] + nxt * W + lanes[r * W + W:]
+                succ.append((rounds2, lanes2, pad))
+        # quiescence: every rank between rounds (all lanes of its current round
+        # still at SEND, or finished) and all at the same round -> pads zero
+        quiet = all(rounds[r] > K or all(lanes[r * W + s] == SEND for s in range(W)) for r in range(W))
+        if quiet and len(set(rounds)) == 1 and any(pad):
+            return CheckResult(False, len(seen), f"pad not zero between barriers: {pad}")
+        if not succ:
+            if not all(x == K + 1 for x in rounds):
+                return CheckResult(False, len(seen), f"deadlock: rounds {rounds} lanes {lanes} pad {pad}")
+            if any(pad):
+                return CheckResult(False, len(seen), f"pad not zero after the last barrier: {pad}")
+            finals += 1
+        for s2 in succ:
+            if s2 not in seen:
+                seen.add(s2)
+                stack.append(s2)
+                if len(seen) > max_states:
+                    raise RuntimeError(f"state space exceeds {max_states}")
+    return CheckResult(True, len(seen), None, finals)
+
+
+def barrier_pads_after(W: int, nblocks: int, rounds: int = 1) -> List[np.ndarray]:
+    """Expected pads after `rounds` complete barriers on every block id from
+    zero-filled pads: all zero (page "triton_barrier.py", blockwise_barrier
+    docstring on graph friendliness)."""
+    return [np.zeros((nblocks, W), np.uint32) for _ in range(W)]

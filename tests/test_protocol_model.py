@@ -1,0 +1,101 @@
+"""Pins for the protocol oracle (CPU only).
+
+The brute-force checkers must accept the protocol as the pages state it and
+reject each mutant that drops one of its safety rules (page "arx.cu":
+protocol comment on parity buffers and in-order posting, the comment on
+separate per-phase counters, and the go wait; page "triton_barrier.py":
+send_signal / wait_signal CAS semantics and the zero-filled pad). The
+sequential single-GPU model is pinned by closed-form final states.
+"""
+import numpy as np
+import pytest
+
+from oracle import protocol as P
+from oracle import reduce as R
+from signal_pad_sync_amd import workloads as WL
+
+SIZES = [(2, 1, 4), (2, 2, 3), (3, 1, 3), (3, 2, 2), (4, 1, 2)]
+
+
+@pytest.mark.parametrize("W,G,S", SIZES)
+def test_protocol_safe_and_live(W, G, S):
+    r = P.check_protocol(W, G, S)
+    assert r.ok, r.violation
+    assert r.finals == 1      # every run ends in the same final state
+
+
+@pytest.mark.parametrize("mutant", ["M1", "M2", "M3", "M4", "M5"])
+def test_each_protocol_mutant_is_caught(mutant):
+    # at least one small configuration must expose every mutant
+    found = [P.check_protocol(W, G, S, mutant=mutant) for W, G, S in [(2, 2, 3), (3, 2, 2)]]
+    assert any(not r.ok for r in found), mutant
+    assert all(r.violation for r in found if not r.ok)
+
+
+def test_mutant_kinds():
+    """Each mutant fails the way the page says it would."""
+    assert "stale" in P.check_protocol(2, 1, 3, mutant="M1").violation   # skipped seq -> stale data
+    assert "stale" in P.check_protocol(2, 1, 3, mutant="M2").violation   # one buffer -> overwritten data
+    assert "stale" in P.check_protocol(2, 1, 3, mutant="M3").violation   # flag before data
+    assert P.check_protocol(2, 2, 3, mutant="M4").violation               # shared counter
+    assert "stale" in P.check_protocol(2, 2, 3, mutant="M5").violation   # no go wait
+
+
+@pytest.mark.parametrize("W,K", [(2, 1), (2, 3), (2, 4), (3, 2), (3, 3)])
+def test_barrier_safe_live_and_zero(W, K):
+    r = P.check_barrier(W, K)
+    assert r.ok, r.violation
+    assert r.finals == 1
+
+
+def test_barrier_mutants_are_caught():
+    b1 = P.check_barrier(2, 2, mutant="B1")
+    assert not b1.ok and "deadlock" in b1.violation       # lost signal
+    b2 = P.check_barrier(2, 2, mutant="B2")
+    assert not b2.ok and "not zero" in b2.violation       # pad left dirty
+    assert not P.check_barrier(3, 2, mutant="B1").ok
+    assert not P.check_barrier(3, 2, mutant="B2").ok
+
+
+def _recv(cfg, W, n):
+    return [WL.recv_partials(cfg, par, n, W) for par in (0, 1)]
+
+
+@pytest.mark.parametrize("mode", [P.LOCKSTEP, P.RUNAHEAD])
+def test_sequential_model_final_state(mode):
+    """K calls leave seq_dev = go = ctl.seq = ctl.done = K, both counters 0,
+    every peer flag at K (lockstep) or K + 1 (run-ahead), this rank's flag
+    untouched, and the send slots holding the inputs of calls K and K - 1."""
+    W, n, K = 8, 4096, 25
+    recv = _recv(2, W, n)
+    calls = [(WL.own_partial(2, k, n), n) for k in range(1, K + 1)]
+    st, outs = P.sequential_model(calls, recv, W, rank=0, mode=mode)
+    assert st.seq_dev == st.go == st.ctl_seq == st.ctl_done == K
+    assert st.cnt == [0, 0]
+    lead = 1 if mode == P.RUNAHEAD else 0
+    assert st.flags == [0] + [K + lead] * (W - 1)
+    assert st.ctl_bytes == [2 * n, 2 * n]
+    assert np.array_equal(st.send[K & 1], calls[K - 1][0])
+    assert np.array_equal(st.send[(K - 1) & 1], calls[K - 2][0])
+    # call k reduces with the recv slots of parity k & 1
+    for k in (1, 2, K):
+        parts = [calls[k - 1][0]] + [recv[k & 1][s] for s in range(1, W)]
+        assert np.array_equal(outs[k - 1], R.reduce(parts, n=n))
+
+
+def test_sequential_model_rank_placement():
+    """With rank r, this GPU's partial takes position r in the sum."""
+    W, n = 4, 1000
+    recv = _recv(3, W, n)
+    x = WL.recv_partials(3, 1, n)[2]
+    st, outs = P.sequential_model([(x, n)], recv, W, rank=2)
+    parts = [recv[1][0], recv[1][1], x, recv[1][3]]
+    assert np.array_equal(outs[0], R.reduce(parts))
+    assert st.flags == [1, 1, 0, 1]
+
+
+def test_sequential_model_manual_needs_flags():
+    W, n = 2, 64
+    recv = _recv(1, W, n)
+    with pytest.raises(RuntimeError):
+        P.sequential_model([(recv[1][0], n)], recv, W, mode=P.MANUAL)
