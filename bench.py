@@ -1,0 +1,247 @@
+"""Benchmark of the one-shot W-way bf16 reduction on one MI355X.
+
+Workload (the headline): W = 8 partials of bf16 [32, 4096] (n = 131072,
+256 KiB each), values N(0,1)*0.1, K consecutive one-shot calls on one
+stream with parity alternating and the virtual peers' flags posted by the
+library's host proxy thread into pinned memory (lockstep). One step = one
+call: copy into the send slot, publish, flag wait, go broadcast, W-way
+reduction, last-block-out. Inputs are resident in HBM before timing.
+
+value = algorithmic bytes per call / time per call, with the algorithmic
+bytes (W + 3) * 2n = 2,883,584 B (copy read + write, W reads, one write).
+The same run also measures the reduction alone on W = 8, bf16 [8192, 8192]
+(128 MiB per partial), the run-ahead proxy mode, the blockwise barrier, and
+the CPU oracle on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "one-shot reduce GB/s (% of HBM peak) + µs/call at W=8, 256 KB bf16"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--reduce-reps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of phases: oneshot,runahead,graph,reduce,barrier")
+    return ap.parse_args()
+
+
+def timed(fn, steps, stream):
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3  # microseconds
+
+
+def bench_oneshot(args, mode, graph=False):
+    """K one-shot calls at W=8, n=131072; returns microseconds per call."""
+    import numpy as np
+    import torch
+    from signal_pad_sync_amd import arx
+    from signal_pad_sync_amd import workloads as WL
+
+    W, n = 8, 131072
+    arx.init(W, n)
+    try:
+        arx.set_proxy_mode(mode)
+        for par in (0, 1):
+            parts = WL.recv_partials(2, par, n)
+            for src in range(1, W):
+                arx.recv_view(par, src, n).copy_(torch.from_numpy(parts[src].view(np.int16)).cuda().view(torch.bfloat16))
+        x = torch.from_numpy(WL.own_partial(2, 1, n).view(np.int16)).cuda().view(torch.bfloat16)
+        out = torch.empty_like(x)
+        stream = torch.cuda.current_stream()
+        if graph:
+            per = 100
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(per):
+                    arx.allreduce(x, out, n)
+            fn, reps = g.replay, max(1, args.steps // per)
+        else:
+            per = 1
+            fn, reps = (lambda: arx.allreduce(x, out, n)), args.steps
+        for _ in range(max(1, args.warmup // per)):
+            fn()
+        us = timed(fn, reps, stream)
+        calls = reps * per
+        st = arx.debug_state()
+        assert st["ctl_err"] == 0 and st["cnt0"] == 0 and st["cnt1"] == 0, st
+    finally:
+        torch.cuda.synchronize()
+        arx.finalize()
+    return us / calls, calls
+
+
+def bench_reduce(args):
+    """Reduction alone at W=8, n = 8192*8192; returns microseconds per call."""
+    import torch
+    from signal_pad_sync_amd import arx
+
+    W, n = 8, 8192 * 8192
+    arx.init(W, n)
+    try:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(4000)
+        for par in (0, 1):
+            for src in range(1, W):
+                v = arx.recv_view(par, src, n)
+                v.copy_(torch.randn(n, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16))
+        x = torch.randn(n, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        out = torch.empty_like(x)
+        stream = torch.cuda.current_stream()
+        k = [0]
+
+        def step():
+            arx.reduce(x, out, k[0] & 1, n)
+            k[0] += 1
+
+        for _ in range(3):
+            step()
+        samples = [timed(step, 1, stream) for _ in range(args.reduce_reps)]
+        us_total = timed(step, args.reduce_reps, stream)
+    finally:
+        torch.cuda.synchronize()
+        arx.finalize()
+    samples.sort()
+    return samples[len(samples) // 2], us_total / args.reduce_reps
+
+
+def bench_barrier(args):
+    import torch
+    from signal_pad_sync_amd import arx
+    arx.init(8, 1024)
+    try:
+        stream = torch.cuda.current_stream()
+        fn = lambda: arx.barrier_blockwise(256, arx.SEM_ACQ_REL, 1)
+        for _ in range(args.warmup):
+            fn()
+        us = timed(fn, args.steps, stream)
+        for r in range(8):
+            assert int(arx.pad_view(r).abs().sum()) == 0
+    finally:
+        torch.cuda.synchronize()
+        arx.finalize()
+    return us / args.steps
+
+
+def cpu_baseline(seconds):
+    """The oracle's one-shot model (sequential protocol + C reduction) on the
+    headline workload, single-threaded, for about `seconds` of CPU time."""
+    from oracle import protocol as P
+    from signal_pad_sync_amd import workloads as WL
+
+    W, n = 8, 131072
+    recv = [WL.recv_partials(2, par, n) for par in (0, 1)]
+    x = WL.own_partial(2, 1, n)
+    st = None
+    t0 = time.perf_counter()
+    st, _ = P.sequential_model([(x, n)] * 10, recv, W)
+    per = (time.perf_counter() - t0) / 10
+    calls = max(10, int(seconds / per))
+    t0 = time.perf_counter()
+    st, _ = P.sequential_model([(x, n)] * calls, recv, W)
+    dt = time.perf_counter() - t0
+    return calls, dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the one-shot reduction; the virtual peers live on the "
+              "same GPU, so --gpus must be 1 (no multi-GPU run exists in this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from signal_pad_sync_amd import arx
+
+    torch.cuda.set_device(0)
+    only = set(filter(None, args.only.split(",")))
+    want = lambda p: not only or p in only
+    W, n = 8, 131072
+    bytes_call = (W + 3) * 2 * n
+    extra = {}
+
+    us_call = None
+    if want("oneshot"):
+        log("one-shot, lockstep proxy")
+        us_call, calls = bench_oneshot(args, arx.PROXY_LOCKSTEP)
+        log(f"  {us_call:.2f} us/call over {calls} calls")
+    if want("runahead"):
+        log("one-shot, run-ahead proxy")
+        us_ra, _ = bench_oneshot(args, arx.PROXY_RUNAHEAD)
+        extra["runahead_us_per_call"] = round(us_ra, 3)
+        log(f"  {us_ra:.2f} us/call")
+    if want("graph"):
+        log("one-shot, lockstep proxy, 100 calls per hipGraph")
+        us_g, _ = bench_oneshot(args, arx.PROXY_LOCKSTEP, graph=True)
+        extra["graph_us_per_call"] = round(us_g, 3)
+        log(f"  {us_g:.2f} us/call")
+    if want("reduce"):
+        log("reduction alone, W=8, bf16 [8192, 8192]")
+        med, mean = bench_reduce(args)
+        rb = (8 + 1) * 2 * 8192 * 8192
+        extra["reduce_128MiB"] = {
+            "workload": "W=8, bf16 [8192,8192] per partial, reduction alone",
+            "bytes_per_call": rb, "us_median": round(med, 2), "us_mean_back_to_back": round(mean, 2),
+            "GBps": round(rb / med / 1e3, 1), "frac_of_hbm_peak": round(rb / med / 1e3 / HBM_PEAK_GBS, 4)}
+        log(f"  {med:.1f} us median, {rb / med / 1e3:.0f} GB/s")
+    if want("barrier"):
+        log("blockwise barrier, 256 workgroups, W=8, acq_rel")
+        extra["barrier_256wg_us"] = round(bench_barrier(args), 3)
+        log(f"  {extra['barrier_256wg_us']} us/launch")
+
+    cpu = None
+    if not args.skip_cpu:
+        log(f"oracle on the CPU, ~{args.cpu_seconds} s")
+        calls, dt = cpu_baseline(args.cpu_seconds)
+        cpu = {"value": round(bytes_call * calls / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{calls} one-shot calls (sequential protocol model + C reduction), W=8, n=131072",
+               "us_per_call": round(dt / calls * 1e6, 1)}
+        log(f"  {cpu['us_per_call']} us/call on 1 core")
+
+    value = bytes_call / us_call / 1e3 if us_call else None
+    line = {
+        "metric": METRIC, "value": round(value, 2) if value else None, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_call / 1e3, 6) if us_call else None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "one-shot reduce, W=8, bf16 [32,4096] per partial (n=131072), consecutive calls, "
+                               "parity alternating, lockstep host-proxy flags in pinned memory",
+                   "W": W, "n": n, "io_dtype": "bf16", "accumulate": "f32"},
+        "us_per_call": round(us_call, 3) if us_call else None,
+        "roofline": {"bound": "hbm", "achieved": round(value, 2) if value else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 5) if value else None,
+                     "traffic": None, "kernel": "oneshot_kernel<8,true>", "bytes_per_launch": bytes_call},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

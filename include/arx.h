@@ -1,0 +1,197 @@
+/*
+ * arx.h — C ABI of libarx: the one-shot W-way bf16 reduction gated by a
+ * seq/parity flag protocol, and the blockwise signal-pad barrier, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "arx.cu", protocol comment and arx_kernel): this GPU
+ * is rank `rank` of a group of W ranks. A call with sequence number
+ * seq = previous + 1 and parity par = seq & 1
+ *   1. copies the caller's bf16 partial `in` into the send slot send[par],
+ *   2. publishes seq (a host proxy thread sees it and posts the peers' flags),
+ *   3. waits until the flag of every other rank has reached seq,
+ *   4. writes out[i] = bf16(sum over src = 0..W-1, in that order, of the
+ *      binary32 value of partial src at i), where partial `rank` is `in` and
+ *      partial src != rank is recv[par][src]; the sum is accumulated in
+ *      binary32 and rounded once to bf16, round to nearest, ties to even,
+ *      every NaN result written as 0x7FC0, subnormals kept,
+ *   5. resets its own counters, so calls can be captured in a hipGraph.
+ * Every rank running the same calls gets the same bits.
+ *
+ * On one GPU the W - 1 peers are virtual: their partials already sit in the
+ * recv slots of this library (the caller fills them through arx_recv_ptr),
+ * and their flags are posted into pinned host memory by the library's proxy
+ * thread (or by the caller in manual mode). Nothing crosses GPUs.
+ *
+ * Conventions for every call below:
+ *   - return value: ARX_OK (0) or a negative ARX_E* code; the library never
+ *     exits the process; arx_strerror() gives the message of the last error.
+ *   - device pointers are HIP device addresses; host pointers are ordinary
+ *     process memory. The caller owns `in`, `out` and the stream; the library
+ *     owns every slot, flag, counter, pad and its proxy thread.
+ *   - the library keeps one instance per process and is not thread-safe:
+ *     issue all calls from one thread, in order on one stream (seq is a
+ *     running counter kept on the device).
+ */
+#ifndef ARX_H
+#define ARX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define ARX_OK 0
+#define ARX_EINVAL (-1)   /* bad argument: world, rank, n, alignment, null pointer */
+#define ARX_ESTATE (-2)   /* not initialised, or initialised twice */
+#define ARX_ENOMEM (-3)   /* device or pinned allocation failed */
+#define ARX_EHIP (-4)     /* a HIP runtime call failed (message kept for arx_strerror) */
+#define ARX_EPROXY (-5)   /* the proxy thread failed earlier (latched) */
+#define ARX_EORDER (-6)   /* arx_publish called with a seq that is not last + 1 */
+#define ARX_ETIMEOUT (-7) /* a kernel's bounded wait ran out (latched until finalize) */
+
+/* Limits. */
+#define ARX_MAX_WORLD 8          /* page "arx.cu": kMaxWorld; page "common.cuh": kMaxNumGPU */
+#define ARX_MAX_PAD_BLOCKS 1024  /* workgroups per barrier launch */
+#define ARX_MAX_N ((size_t)1 << 30) /* elements per partial */
+
+/* Proxy modes: when the virtual peers post the flag of seq s. */
+#define ARX_PROXY_LOCKSTEP 0 /* once this rank has published s (peers exactly as fast) */
+#define ARX_PROXY_RUNAHEAD 1 /* once this rank has published s - 1 (the earliest a peer can) */
+#define ARX_PROXY_MANUAL 2   /* never; the caller calls arx_publish */
+
+/* Barrier memory semantics (page "triton_barrier.py", blockwise_barrier). */
+#define ARX_SEM_RELAXED 0 /* relaxed system-scope CAS on both sides */
+#define ARX_SEM_ACQ_REL 1 /* release CAS to signal, acquire CAS to consume */
+
+/*
+ * arx_init — allocate and zero all state, start the proxy thread.
+ * Page "arx.cu": arx_prepare (world range check, pinned flag and control
+ * blocks, zeroed) and arx_connect (device seq/counter/go words zeroed, proxy
+ * thread started). This GPU is rank 0.
+ *   world: W in [2, 8].  max_n: largest n any later call may use, in bf16
+ *   elements, 1 <= max_n <= ARX_MAX_N.
+ * Allocates on the current HIP device: send slots [2][max_n] and recv slots
+ * [2][W][max_n] bf16 in device memory, W signal pads u32[ARX_MAX_PAD_BLOCKS][W],
+ * the device words (seq, two counters, go, abort), and in pinned coherent
+ * host memory the control block and flags[W] (u64). Errors: ARX_EINVAL,
+ * ARX_ESTATE (already initialised), ARX_ENOMEM, ARX_EHIP.
+ */
+int arx_init(int world, size_t max_n);
+
+/* arx_init with an explicit rank in [0, world): this GPU's partial then takes
+ * position `rank` in the sum and the proxy posts flags for every other rank. */
+int arx_init_rank(int world, size_t max_n, int rank);
+
+/* Stop the proxy thread (page "arx.cu": the stop word of struct Ctl), wait
+ * for the device, free everything. Allowed only when initialised; a later
+ * arx_init starts afresh with seq 0. */
+int arx_finalize(void);
+
+/*
+ * arx_publish — the virtual peers publish seq: store-release flags[src] = seq
+ * for every src != rank into pinned memory. seq must be exactly the last
+ * posted seq + 1 (page "arx.cu": the proxy posts every seq in order, since a
+ * skipped seq would let a peer accept a later flag over stale data);
+ * otherwise ARX_EORDER and nothing is written. Called by the proxy thread in
+ * the lockstep and run-ahead modes, by the caller in manual mode.
+ */
+int arx_publish(uint64_t seq);
+
+/*
+ * arx_allreduce — one call of the one-shot path (page "arx.cu": arx_kernel,
+ * arx_allreduce). Launches one kernel on `stream`, asynchronously; the call
+ * is hipGraph-capturable (each replay is the next seq).
+ *   in:  device bf16 [n], this rank's partial, 16-byte aligned.
+ *   out: device bf16 [n], 16-byte aligned; may alias `in`. out[i >= n] is
+ *        never written.
+ *   n:   0 <= n <= max_n, any value (n % 8 != 0 allowed); n == 0 still runs
+ *        the protocol and advances seq.
+ * Errors (nothing launched): ARX_ESTATE, ARX_EINVAL, ARX_EPROXY (proxy failed
+ * earlier), ARX_ETIMEOUT (an earlier call's wait timed out), ARX_EHIP.
+ * If this call's own flag wait times out on the device, out is left
+ * untouched, seq still advances and the error is latched for the next call.
+ */
+int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream);
+
+/*
+ * arx_reduce — the reduction step alone, no copy, publish or wait: out[i] =
+ * rank-ordered sum of `in` (at position rank) and recv[par][src] (src !=
+ * rank), as in arx_allreduce. par in {0, 1}. Same pointer and n rules as
+ * arx_allreduce; does not touch seq, counters or flags.
+ */
+int arx_reduce(const void* in, void* out, size_t n, int par, hipStream_t stream);
+
+/*
+ * arx_barrier_blockwise — launch `nblocks` workgroups; workgroup b runs the
+ * blockwise signal-pad barrier on block id b for all W virtual ranks (page
+ * "triton_barrier.py": blockwise_barrier, send_signal, wait_signal): wave v
+ * plays rank v, its lane s < W CASes slot v of block b in rank s's pad from
+ * 0 to 1 and then CASes slot s of block b in its own pad from 1 to 0. The
+ * pads start zero-filled and are zero-filled again after every barrier, so
+ * the launch is hipGraph-capturable with no host reset.
+ *   nblocks: 1..ARX_MAX_PAD_BLOCKS.  sem: ARX_SEM_RELAXED or ARX_SEM_ACQ_REL.
+ *   rounds: consecutive barriers per workgroup, 1..64.
+ * Errors: ARX_ESTATE, ARX_EINVAL, ARX_ETIMEOUT (latched), ARX_EHIP.
+ */
+int arx_barrier_blockwise(int nblocks, int sem, int rounds, hipStream_t stream);
+
+/* Device address of recv slot [par][src] (max_n bf16), where the caller puts
+ * peer src's partial for parity par; NULL if not initialised or out of range
+ * (par not in {0,1}, src not in [0, W)). The slot at src == rank is unused. */
+void* arx_recv_ptr(int par, int src);
+
+/* Device address of send slot [par] (max_n bf16); NULL as above. */
+void* arx_send_ptr(int par);
+
+/* Device address of virtual rank `rank`'s signal pad, u32[ARX_MAX_PAD_BLOCKS][W]
+ * (block b, slot s at b * W + s); NULL as above. */
+uint32_t* arx_pad_ptr(int rank);
+
+/* Choose when the proxy posts flags (ARX_PROXY_*). Change it only while no
+ * call is in flight. */
+int arx_set_proxy_mode(int mode);
+
+/* Bound of every device-side wait, in microseconds (default 2000000, i.e.
+ * 2 s; 1 us .. 60 s). Applies to calls launched after it. */
+int arx_set_timeout_us(uint64_t us);
+
+/* Watchdog view (page "arx.cu": the STALL report of proxy_loop): last seq
+ * published by this GPU, last seq posted for the peers, last seq whose
+ * reduction finished. Any pointer may be NULL. */
+int arx_status(uint64_t* published, uint64_t* posted, uint64_t* done);
+
+/*
+ * arx_debug_state — copy every protocol word, synchronously (waits for the
+ * device), into words[0..nwords): [0] seq_dev, [1] arrival counter,
+ * [2] finish counter, [3] go, [4] abort, [5] ctl.seq, [6] ctl.bytes[0],
+ * [7] ctl.bytes[1], [8] ctl.done, [9] ctl.err, [10] ctl.err_seq,
+ * [11] posted, [12 .. 12+W) flags[src]. Returns the number of words written.
+ */
+int arx_debug_state(uint64_t* words, int nwords);
+
+/* The binary32 -> bf16 rounding of the reduction alone (for exhaustive
+ * checks): out[i] = the bf16 pattern the reduction writes for the binary32
+ * pattern in[i]. in: device u32 [n], out: device u16 [n]; n <= 2^32 - 1. */
+int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream);
+
+/* Message for an error code; for the last failing call, the message includes
+ * its detail (a HIP error string, the offending argument). */
+const char* arx_strerror(int err);
+
+/* max_n given to arx_init (0 if not initialised); page "arx.cu": arx_max_bytes. */
+size_t arx_max_n(void);
+
+/* W and this GPU's rank (0 if not initialised). */
+int arx_world(void);
+int arx_rank(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARX_H */

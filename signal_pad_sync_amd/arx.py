@@ -1,0 +1,188 @@
+"""ctypes binding of libarx.so (C ABI in include/arx.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. torch provides device memory and streams; tensors are passed as
+``data_ptr()`` and streams as ``torch.cuda.current_stream().cuda_stream``.
+Importing this module raises if libarx.so is missing: there is no fallback.
+"""
+import atexit
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarx.so")
+
+OK, EINVAL, ESTATE, ENOMEM, EHIP, EPROXY, EORDER, ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
+PROXY_LOCKSTEP, PROXY_RUNAHEAD, PROXY_MANUAL = 0, 1, 2
+SEM_RELAXED, SEM_ACQ_REL = 0, 1
+MAX_WORLD, MAX_PAD_BLOCKS, MAX_N = 8, 1024, 1 << 30
+
+# names of arx_debug_state's words, in order
+STATE_WORDS = ["seq_dev", "cnt0", "cnt1", "go", "abort", "ctl_seq", "ctl_bytes0", "ctl_bytes1",
+               "ctl_done", "ctl_err", "ctl_err_seq", "posted"]
+
+_c = ctypes
+_u64p = _c.POINTER(_c.c_uint64)
+
+# (name, restype, argtypes) for every entry point of arx.h
+SIGNATURES = [
+    ("arx_init", _c.c_int, [_c.c_int, _c.c_size_t]),
+    ("arx_init_rank", _c.c_int, [_c.c_int, _c.c_size_t, _c.c_int]),
+    ("arx_finalize", _c.c_int, []),
+    ("arx_publish", _c.c_int, [_c.c_uint64]),
+    ("arx_allreduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    ("arx_reduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_void_p]),
+    ("arx_barrier_blockwise", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
+    ("arx_recv_ptr", _c.c_void_p, [_c.c_int, _c.c_int]),
+    ("arx_send_ptr", _c.c_void_p, [_c.c_int]),
+    ("arx_pad_ptr", _c.c_void_p, [_c.c_int]),
+    ("arx_set_proxy_mode", _c.c_int, [_c.c_int]),
+    ("arx_set_timeout_us", _c.c_int, [_c.c_uint64]),
+    ("arx_status", _c.c_int, [_u64p, _u64p, _u64p]),
+    ("arx_debug_state", _c.c_int, [_u64p, _c.c_int]),
+    ("arx_test_round_bf16", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    ("arx_strerror", _c.c_char_p, [_c.c_int]),
+    ("arx_max_n", _c.c_size_t, []),
+    ("arx_world", _c.c_int, []),
+    ("arx_rank", _c.c_int, []),
+]
+
+
+class ArxError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"arx error {code}: {msg}")
+        self.code = code
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libarx.so not found at {path}; build it with signal_pad_sync_amd/build.py")
+    L = ctypes.CDLL(path)
+    for name, res, args in SIGNATURES:
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = load()
+
+
+@atexit.register
+def _finalize_at_exit():
+    if lib.arx_world() != 0:
+        lib.arx_finalize()
+
+
+def _check(rc):
+    if rc < 0:
+        raise ArxError(rc, lib.arx_strerror(rc).decode())
+    return rc
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def init(world: int, max_n: int, rank: int = 0):
+    _check(lib.arx_init_rank(world, max_n, rank))
+
+
+def finalize():
+    _check(lib.arx_finalize())
+
+
+def publish(seq: int):
+    _check(lib.arx_publish(seq))
+
+
+def allreduce(inp, out, n: int = None, stream=None):
+    """One one-shot call: out[:n] = rank-ordered sum; inp/out bf16 tensors."""
+    if n is None:
+        n = inp.numel()
+    _check(lib.arx_allreduce(_ptr(inp), _ptr(out), n, _stream(stream)))
+
+
+def reduce(inp, out, par: int, n: int = None, stream=None):
+    if n is None:
+        n = inp.numel()
+    _check(lib.arx_reduce(_ptr(inp), _ptr(out), n, par, _stream(stream)))
+
+
+def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, stream=None):
+    _check(lib.arx_barrier_blockwise(nblocks, sem, rounds, _stream(stream)))
+
+
+def set_proxy_mode(mode: int):
+    _check(lib.arx_set_proxy_mode(mode))
+
+
+def set_timeout_us(us: int):
+    _check(lib.arx_set_timeout_us(us))
+
+
+def status():
+    a, b, c = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib.arx_status(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def debug_state() -> dict:
+    buf = (ctypes.c_uint64 * 32)()
+    m = _check(lib.arx_debug_state(buf, 32))
+    d = {name: buf[i] for i, name in enumerate(STATE_WORDS)}
+    d["flags"] = [buf[i] for i in range(len(STATE_WORDS), m)]
+    return d
+
+
+def max_n() -> int:
+    return lib.arx_max_n()
+
+
+def world() -> int:
+    return lib.arx_world()
+
+
+def test_round_bf16(inp_u32, out_u16, stream=None):
+    _check(lib.arx_test_round_bf16(_ptr(inp_u32), _ptr(out_u16), inp_u32.numel(), _stream(stream)))
+
+
+class _DevArray:
+    """__cuda_array_interface__ view of library-owned device memory."""
+
+    def __init__(self, ptr, n, typestr):
+        self.__cuda_array_interface__ = {"shape": (n,), "typestr": typestr, "data": (ptr, False),
+                                         "version": 2, "strides": None}
+
+
+def _view(ptr, n, typestr, dtype):
+    import torch
+    if not ptr:
+        raise ArxError(EINVAL, "null slot (library not initialised or index out of range)")
+    t = torch.as_tensor(_DevArray(ptr, n, typestr), device="cuda")
+    return t.view(dtype) if dtype is not None else t
+
+
+def recv_view(par: int, src: int, n: int = None):
+    """bf16 tensor viewing recv slot [par][src] (library memory, no copy)."""
+    import torch
+    return _view(lib.arx_recv_ptr(par, src), n or max_n(), "<i2", torch.bfloat16)
+
+
+def send_view(par: int, n: int = None):
+    import torch
+    return _view(lib.arx_send_ptr(par), n or max_n(), "<i2", torch.bfloat16)
+
+
+def pad_view(rank: int):
+    """int32 tensor viewing virtual rank `rank`'s pad, shape [MAX_PAD_BLOCKS, W]."""
+    W = world()
+    return _view(lib.arx_pad_ptr(rank), MAX_PAD_BLOCKS * W, "<i4", None).view(MAX_PAD_BLOCKS, W)

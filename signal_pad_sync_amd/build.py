@@ -1,0 +1,37 @@
+"""Builds libarx.so (HIP for gfx950) in-tree with hipcc.
+
+Floating-point flags: no contraction (the sum is adds only, in rank order),
+fp32 denormals kept on the GPU, and packed-fp32 instructions disabled. The
+host compile pass warns that it does not know the last feature; that is
+harmless.
+"""
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libarx.so")
+SOURCES = [os.path.join(CSRC, "arx_kernels.hip"), os.path.join(CSRC, "arx_runtime.cpp")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", LIB + ".tmp", "-lpthread"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,90 @@
+// arx_internal.h — layouts and launchers shared by the kernels and the host
+// runtime of libarx (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace arx {
+
+// Control block in pinned, coherent host memory (page "arx.cu": struct Ctl).
+// Line 0 is written by the GPU when it publishes and read by the proxy;
+// line 1 is written by the GPU when a call finishes or a wait times out;
+// line 2 is host-only.
+struct alignas(64) Ctl {
+  uint64_t seq;       // last seq this GPU published
+  uint64_t bytes[2];  // bytes of the partial in send[parity]
+  uint64_t pad0[5];
+  uint64_t done;      // last seq whose reduction finished
+  uint64_t err;       // first device-side error kind (ERR_*), 0 if none
+  uint64_t err_seq;   // seq of that error
+  uint64_t pad1[5];
+  uint64_t stop;      // asks the proxy thread to return
+  uint64_t pad2[7];
+};
+static_assert(sizeof(Ctl) == 192, "Ctl layout");
+
+enum : uint64_t {
+  ERR_NONE = 0,
+  ERR_FLAG_TIMEOUT = 1,     // workgroup 0 gave up waiting for a peer flag
+  ERR_GO_TIMEOUT = 2,       // a workgroup gave up waiting for go
+  ERR_BARRIER_TIMEOUT = 3,  // a signal-pad CAS wait gave up
+};
+
+// Device words (u32), each on its own 256-byte line of one allocation.
+enum : int {
+  WORD_SEQ = 0,      // last completed seq
+  WORD_CNT0 = 64,    // workgroups past the copy (arrival counter)
+  WORD_CNT1 = 128,   // workgroups finished (finish counter)
+  WORD_GO = 192,     // seq whose peer data has all arrived
+  WORD_ABORT = 256,  // seq whose wait timed out (its reduction is skipped)
+  WORDS_TOTAL = 1024,
+};
+
+constexpr int kBlock = 256;       // threads per workgroup of the reduction kernels
+constexpr int kMaxOneShotGrid = 256;  // co-resident workgroups of the one-shot kernel
+
+struct OneShotArgs {
+  const uint16_t* in;
+  uint16_t* out;
+  uint16_t* send;          // send slot 0; slot 1 at + stride
+  const uint16_t* recv;    // [2][W][stride]
+  uint64_t stride;         // elements per slot
+  const uint64_t* flags;   // pinned [W]
+  Ctl* ctl;                // pinned
+  uint32_t* words;         // device
+  uint32_t n;
+  int rank;
+  uint64_t timeout;        // wall-clock ticks per wait
+};
+
+struct ReduceArgs {
+  const uint16_t* in;
+  uint16_t* out;
+  const uint16_t* recv_par;  // recv slots of the chosen parity: [W][stride]
+  uint64_t stride;
+  uint32_t n;
+  int rank;
+};
+
+struct BarrierArgs {
+  uint32_t* pad[8];
+  int world;
+  int acq_rel;
+  int rounds;
+  uint64_t timeout;
+  Ctl* ctl;
+};
+
+// Launchers (defined in arx_kernels.hip). W in [2, 8].
+hipError_t launch_oneshot(const OneShotArgs& a, int W, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t stream);
+hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t stream);
+hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t stream);
+
+// Grid the one-shot kernel uses for n elements (all its workgroups must be
+// resident at once, since they wait on each other).
+unsigned oneshot_grid(uint32_t n);
+
+}  // namespace arx

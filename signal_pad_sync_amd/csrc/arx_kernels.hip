@@ -1,0 +1,332 @@
+// arx_kernels.hip — the HIP kernels of libarx for gfx950.
+//
+//   oneshot_kernel  one call of the one-shot path: copy into the send slot,
+//                   arrival count and publish, flag wait in workgroup 0, go
+//                   broadcast, W-way reduction, last-block-out (page
+//                   "arx.cu", arx_kernel)
+//   reduce_kernel   the W-way reduction alone, streaming from HBM
+//   barrier_kernel  the blockwise signal-pad barrier for W virtual ranks
+//                   (page "triton_barrier.py", blockwise_barrier)
+//   round_test_kernel  the reduction's binary32 -> bf16 rounding alone
+//
+// Data layout in HBM: send slots [2][stride] bf16, recv slots [2][W][stride]
+// bf16 (stride = max_n rounded up to 128 elements, so every slot starts on a
+// 256-byte boundary); element i of a slot is at byte 2 * i. A thread moves
+// 8 bf16 (16 bytes) per access: lanes of a wave touch 1 KiB of consecutive
+// bytes per instruction.
+#include <hip/hip_runtime.h>
+
+#include "arx_device.h"
+#include "arx_internal.h"
+
+namespace arx {
+
+// ---- buffer loads with an explicit cache policy ---------------------------
+
+// Cache-policy bits of a gfx950 buffer instruction: sc0 = 1, nt = 2, sc1 = 16.
+enum : int {
+  CP_SYS = 1 | 16,  // sc0 sc1: coherent at system scope, no stale cached copy
+  CP_NT = 2,        // nontemporal: streamed, not kept in the caches
+};
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, stride 0; loads
+// past `bytes` return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int CP>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, CP);
+}
+
+template <int CP>
+__device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, CP);
+}
+
+__device__ __forceinline__ uint32_t slot_bytes(uint64_t stride) {
+  return (uint32_t)(stride * 2u);
+}
+
+// ---- one-shot kernel --------------------------------------------------------
+
+// Reports a device-side wait timeout to the host through the pinned control
+// block (first writer wins only loosely: any writer leaves a valid report).
+__device__ __forceinline__ void report_error(Ctl* ctl, uint64_t kind, uint64_t seq) {
+  store_relaxed_system(&ctl->err_seq, seq);
+  store_release_system(&ctl->err, kind);
+}
+
+// ONE_PASS: the grid has a thread for every 16-byte vector, so each thread
+// keeps its own partial's vector in registers from the copy to the sum.
+template <int W, bool ONE_PASS>
+__global__ __launch_bounds__(kBlock) void oneshot_kernel(OneShotArgs a) {
+  __shared__ uint32_t s_abort;
+  uint32_t* const seq_dev = a.words + WORD_SEQ;
+  uint32_t* const cnt0 = a.words + WORD_CNT0;
+  uint32_t* const cnt1 = a.words + WORD_CNT1;
+  uint32_t* const go = a.words + WORD_GO;
+  uint32_t* const abort_w = a.words + WORD_ABORT;
+
+  // seq and parity: one more than the last completed call
+  const uint32_t seq = load_relaxed_agent(seq_dev) + 1u;
+  const uint32_t par = seq & 1u;
+  uint16_t* const mine = a.send + (size_t)par * a.stride;
+  const uint32_t nv = a.n >> 3, tail = a.n & 7u;
+  const uint32_t tid = blockIdx.x * kBlock + threadIdx.x;
+  const uint32_t nthr = gridDim.x * kBlock;
+
+  // 1. copy this rank's partial into send[par]
+  u32x4 own = {0u, 0u, 0u, 0u};
+  if (ONE_PASS) {
+    if (tid < nv) {
+      own = ld16(a.in + 8u * (size_t)tid);
+      st16(mine + 8u * (size_t)tid, own);
+    }
+  } else {
+    for (uint32_t v = tid; v < nv; v += nthr) st16(mine + 8u * (size_t)v, ld16(a.in + 8u * (size_t)v));
+  }
+  if (tid < tail) mine[8u * (size_t)nv + tid] = a.in[8u * (size_t)nv + tid];
+  // every wave's copy is complete and written back before its workgroup counts in
+  fence_release_system();
+  __syncthreads();
+
+  // 2. arrival count; the last workgroup to arrive resets the counter and
+  //    publishes seq to the host proxy
+  if (threadIdx.x == 0) {
+    if (fetch_add_acq_rel_agent(cnt0, 1u) == gridDim.x - 1u) {
+      store_relaxed_agent(cnt0, 0u);
+      store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
+      store_release_system(&a.ctl->seq, (uint64_t)seq);
+    }
+  }
+
+  // 3. workgroup 0 waits for every peer's flag to reach seq, then releases
+  //    the other workgroups through the go word; they wait on go only, so
+  //    just a few lanes poll the pinned flags over PCIe
+  bool abort;
+  if (blockIdx.x == 0) {
+    bool ok = true;
+    if ((int)threadIdx.x < W && (int)threadIdx.x != a.rank) {
+      const uint64_t t0 = now_ticks();
+      while (load_relaxed_system(a.flags + threadIdx.x) < (uint64_t)seq) {
+        if (now_ticks() - t0 > a.timeout) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    fence_acquire_system();
+    const int bad = __syncthreads_or(!ok);
+    if (threadIdx.x == 0) {
+      if (bad) {
+        store_relaxed_agent(abort_w, seq);
+        report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
+      }
+      store_release_agent(go, seq);
+    }
+    abort = bad != 0;
+  } else {
+    if (threadIdx.x == 0) {
+      const uint64_t t0 = now_ticks();
+      bool timed = false;
+      while ((int32_t)(load_relaxed_agent(go) - seq) < 0) {
+        if (now_ticks() - t0 > 2u * a.timeout) {
+          timed = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      fence_acquire_agent();
+      if (timed) report_error(a.ctl, ERR_GO_TIMEOUT, seq);
+      s_abort = (timed || load_relaxed_agent(abort_w) == seq) ? 1u : 0u;
+    }
+    __syncthreads();
+    abort = s_abort != 0u;
+  }
+
+  // 4. rank-ordered W-way sum; peer slots are read with system-coherent
+  //    loads, since another agent wrote them
+  if (!abort) {
+    __amdgpu_buffer_rsrc_t rs[W];
+#pragma unroll
+    for (int src = 0; src < W; ++src)
+      rs[src] = make_rsrc(a.recv + ((size_t)par * W + src) * a.stride, slot_bytes(a.stride));
+    if (ONE_PASS) {
+      if (tid < nv) {
+        u32x4 x[W];
+#pragma unroll
+        for (int src = 0; src < W; ++src)
+          x[src] = (src == a.rank) ? own : bload16<CP_SYS>(rs[src], tid * 16u);
+        st16(a.out + 8u * (size_t)tid, sum_bf16x8<W>(x));
+      }
+    } else {
+      for (uint32_t v = tid; v < nv; v += nthr) {
+        u32x4 x[W];
+#pragma unroll
+        for (int src = 0; src < W; ++src)
+          x[src] = (src == a.rank) ? ld16(a.in + 8u * (size_t)v) : bload16<CP_SYS>(rs[src], v * 16u);
+        st16(a.out + 8u * (size_t)v, sum_bf16x8<W>(x));
+      }
+    }
+    if (tid < tail) {
+      const uint32_t i = 8u * nv + tid;
+      uint16_t x[W];
+#pragma unroll
+      for (int src = 0; src < W; ++src) x[src] = (src == a.rank) ? a.in[i] : bload2<CP_SYS>(rs[src], i * 2u);
+      a.out[i] = sum_bf16x1<W>(x);
+    }
+  }
+
+  // 5. last block out: reset the finish counter, record the completed seq
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (fetch_add_acq_rel_agent(cnt1, 1u) == gridDim.x - 1u) {
+      store_relaxed_agent(cnt1, 0u);
+      store_relaxed_agent(seq_dev, seq);
+      store_release_system(&a.ctl->done, (uint64_t)seq);
+    }
+  }
+}
+
+unsigned oneshot_grid(uint32_t n) {
+  const uint32_t nv = n >> 3;
+  uint32_t g = (nv + kBlock - 1) / kBlock;
+  if (g < 1) g = 1;
+  if (g > (uint32_t)kMaxOneShotGrid) g = kMaxOneShotGrid;
+  return g;
+}
+
+template <int W>
+static hipError_t launch_oneshot_w(const OneShotArgs& a, hipStream_t s) {
+  const unsigned grid = oneshot_grid(a.n);
+  const bool one_pass = (a.n >> 3) <= grid * (uint32_t)kBlock;
+  if (one_pass)
+    hipLaunchKernelGGL((oneshot_kernel<W, true>), dim3(grid), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((oneshot_kernel<W, false>), dim3(grid), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_oneshot(const OneShotArgs& a, int W, hipStream_t s) {
+  switch (W) {
+    case 2: return launch_oneshot_w<2>(a, s);
+    case 3: return launch_oneshot_w<3>(a, s);
+    case 4: return launch_oneshot_w<4>(a, s);
+    case 5: return launch_oneshot_w<5>(a, s);
+    case 6: return launch_oneshot_w<6>(a, s);
+    case 7: return launch_oneshot_w<7>(a, s);
+    case 8: return launch_oneshot_w<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---- reduction alone, streaming from HBM -------------------------------------
+
+// Workgroup b covers vectors [b * kBlock * U, (b + 1) * kBlock * U); thread t
+// handles vectors base + u * kBlock, u < U, issuing all U * W loads before
+// the first add. Inputs were written before the launch, so the loads are
+// nontemporal (stream through, keep nothing) and so are the stores.
+template <int W, int U>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
+  const uint32_t nv = a.n >> 3, tail = a.n & 7u;
+  const uint32_t base = blockIdx.x * (uint32_t)(kBlock * U) + threadIdx.x;
+  __amdgpu_buffer_rsrc_t rs[W];
+#pragma unroll
+  for (int src = 0; src < W; ++src)
+    rs[src] = (src == a.rank) ? make_rsrc(a.in, a.n * 2u)
+                              : make_rsrc(a.recv_par + (size_t)src * a.stride, slot_bytes(a.stride));
+  u32x4 x[U][W];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t v = base + u * kBlock;
+#pragma unroll
+    for (int src = 0; src < W; ++src) x[u][src] = bload16<CP_NT>(rs[src], v * 16u);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t v = base + u * kBlock;
+    if (v < nv) st16_stream(a.out + 8u * (size_t)v, sum_bf16x8<W>(x[u]));
+  }
+  if (blockIdx.x == 0 && threadIdx.x < tail) {
+    const uint32_t i = 8u * nv + threadIdx.x;
+    uint16_t y[W];
+#pragma unroll
+    for (int src = 0; src < W; ++src) y[src] = bload2<CP_NT>(rs[src], i * 2u);
+    a.out[i] = sum_bf16x1<W>(y);
+  }
+}
+
+constexpr int kReduceU = 2;
+
+template <int W>
+static hipError_t launch_reduce_w(const ReduceArgs& a, hipStream_t s) {
+  const uint32_t nv = a.n >> 3;
+  uint32_t grid = (nv + kBlock * kReduceU - 1) / (kBlock * kReduceU);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((reduce_kernel<W, kReduceU>), dim3(grid), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t s) {
+  switch (W) {
+    case 2: return launch_reduce_w<2>(a, s);
+    case 3: return launch_reduce_w<3>(a, s);
+    case 4: return launch_reduce_w<4>(a, s);
+    case 5: return launch_reduce_w<5>(a, s);
+    case 6: return launch_reduce_w<6>(a, s);
+    case 7: return launch_reduce_w<7>(a, s);
+    case 8: return launch_reduce_w<8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---- blockwise signal-pad barrier for W virtual ranks ----------------------
+
+// Workgroup b has W waves; wave v plays rank v and calls the barrier on block
+// id b with its lanes 0..W-1, `rounds` times. With acq_rel each round follows
+// usage pattern 1 of the page (workgroup barrier, acq_rel barrier, workgroup
+// barrier); relaxed rounds follow pattern 0 (relaxed barrier, workgroup
+// barrier). All waves of a workgroup are resident together, so the waits
+// between them always resolve; the timeout only guards against pads that
+// were not zero-filled.
+__global__ void barrier_kernel(BarrierArgs a) {
+  Pads p;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p.pad[i] = a.pad[i];
+  p.world = a.world;
+  const int v = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int r = 0; r < a.rounds; ++r) {
+    if (a.acq_rel) __syncthreads();
+    const bool ok = barrier_blockwise(p, blockIdx.x, v, lane, a.acq_rel != 0, a.timeout);
+    if (__syncthreads_or(!ok)) {
+      if (threadIdx.x == 0) report_error(a.ctl, ERR_BARRIER_TIMEOUT, (uint64_t)blockIdx.x);
+      return;
+    }
+  }
+}
+
+hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL(barrier_kernel, dim3(nblocks), dim3(64 * a.world), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- the rounding alone ------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void round_test_kernel(const uint32_t* in, uint16_t* out, size_t n) {
+  const size_t stride = (size_t)gridDim.x * kBlock;
+  for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+    out[i] = (uint16_t)(round_bf16_hi(__uint_as_float(in[i])) >> 16);
+}
+
+hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t s) {
+  size_t grid = (n + kBlock - 1) / kBlock;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(round_test_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace arx

@@ -1,0 +1,408 @@
+// arx_runtime.cpp — host side of libarx: state, the proxy thread that posts
+// the virtual peers' flags, argument checks and the C ABI declared in arx.h.
+//
+// Page "arx.cu": arx_prepare / arx_connect allocate and zero the pinned and
+// device state and start the proxy; arx_allreduce checks its arguments and
+// launches the kernel on the caller's stream; proxy_loop watches the
+// published seq, posts every seq in order and reports stalls.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <thread>
+
+#include "arx.h"
+#include "arx_internal.h"
+
+namespace {
+
+using arx::Ctl;
+
+struct State {
+  bool inited = false;
+  int world = 0, rank = 0, device = 0;
+  size_t max_n = 0, stride = 0;
+  uint16_t* send = nullptr;   // device [2][stride]
+  uint16_t* recv = nullptr;   // device [2][W][stride]
+  uint32_t* pads = nullptr;   // device [W][ARX_MAX_PAD_BLOCKS][W]
+  uint32_t* words = nullptr;  // device [WORDS_TOTAL]
+  Ctl* ctl = nullptr;         // pinned, host address
+  uint64_t* flags = nullptr;  // pinned, host address [8]
+  Ctl* ctl_dev = nullptr;     // the same memory, device address
+  uint64_t* flags_dev = nullptr;
+  uint64_t clock_khz = 100000;
+  uint64_t timeout_us = 2000000;
+  std::thread proxy;
+  std::atomic<int> mode{ARX_PROXY_LOCKSTEP};
+  std::atomic<uint64_t> posted{0};
+  std::atomic<bool> proxy_err{false};
+  std::atomic<bool> stop{false};
+  std::atomic<uint64_t> stalls{0};
+  std::mutex publish_mu;
+
+  // A process that never called arx_finalize still must not end with a
+  // joinable thread (that aborts): stop and join the proxy, CPU-side only.
+  ~State() {
+    if (proxy.joinable()) {
+      stop.store(true);
+      proxy.join();
+    }
+  }
+};
+
+State S;
+char g_detail[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define HIPCHK(call)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(ARX_EHIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+inline uint64_t load_acquire(const uint64_t* p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
+inline void store_release(uint64_t* p, uint64_t v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
+
+// The virtual peers publish seq s: every flag but this rank's becomes s.
+int publish_locked(uint64_t s) {
+  const uint64_t last = S.posted.load(std::memory_order_acquire);
+  if (s != last + 1) return fail(ARX_EORDER, "arx_publish(%llu) after %llu: seqs are posted in order",
+                                 (unsigned long long)s, (unsigned long long)last);
+  for (int src = 0; src < S.world; ++src)
+    if (src != S.rank) store_release(&S.flags[src], s);
+  S.posted.store(s, std::memory_order_release);
+  return ARX_OK;
+}
+
+inline void cpu_relax() { __builtin_ia32_pause(); }
+
+// Proxy thread (page "arx.cu", proxy_loop): polls the seq this GPU published
+// and, in the lockstep and run-ahead modes, posts every seq in order up to
+// the target the mode allows. Between posts it acts as the watchdog: work
+// published but not finished for 2 s is reported once, with the peer flags.
+void proxy_loop() {
+  using clk = std::chrono::steady_clock;
+  uint64_t last_done = 0;
+  auto last_move = clk::now();
+  bool reported = false;
+  unsigned spin = 0;
+  while (!S.stop.load(std::memory_order_acquire)) {
+    const uint64_t pub = load_acquire(&S.ctl->seq);
+    const int mode = S.mode.load(std::memory_order_relaxed);
+    const uint64_t posted = S.posted.load(std::memory_order_acquire);
+    uint64_t target = posted;
+    if (mode == ARX_PROXY_LOCKSTEP) target = pub;
+    else if (mode == ARX_PROXY_RUNAHEAD) target = pub + 1;
+    if (target > posted) {
+      std::lock_guard<std::mutex> g(S.publish_mu);
+      for (uint64_t s = S.posted.load() + 1; s <= target; ++s)
+        if (publish_locked(s) != ARX_OK) {
+          fprintf(stderr, "arx rank %d: proxy failed to post seq %llu\n", S.rank, (unsigned long long)s);
+          S.proxy_err.store(true);
+          return;
+        }
+      continue;
+    }
+    if ((++spin & 1023u) == 0) {
+      const uint64_t done = load_acquire(&S.ctl->done);
+      const auto now = clk::now();
+      if (done != last_done || done >= pub) {
+        last_done = done;
+        last_move = now;
+        reported = false;
+      } else if (!reported && now - last_move > std::chrono::seconds(2)) {
+        reported = true;
+        S.stalls.fetch_add(1);
+        char buf[512];
+        int o = snprintf(buf, sizeof buf, "arx rank %d STALL: published %llu posted %llu done %llu; flags:", S.rank,
+                         (unsigned long long)pub, (unsigned long long)posted, (unsigned long long)done);
+        for (int j = 0; j < S.world && o < (int)sizeof buf; ++j)
+          if (j != S.rank)
+            o += snprintf(buf + o, sizeof buf - o, " r%d=%llu", j, (unsigned long long)load_acquire(&S.flags[j]));
+        fprintf(stderr, "%s\n", buf);
+      }
+    }
+    cpu_relax();
+  }
+}
+
+int check_ready() {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  if (S.proxy_err.load()) return fail(ARX_EPROXY, "arx proxy thread failed earlier");
+  const uint64_t err = load_acquire(&S.ctl->err);
+  if (err != arx::ERR_NONE)
+    return fail(ARX_ETIMEOUT, "a device wait timed out earlier (kind %llu, seq %llu); finalize and init again",
+                (unsigned long long)err, (unsigned long long)load_acquire(&S.ctl->err_seq));
+  return ARX_OK;
+}
+
+uint64_t timeout_ticks() { return S.timeout_us * S.clock_khz / 1000u; }
+
+void free_all() {
+  if (S.send) (void)hipFree(S.send);
+  if (S.recv) (void)hipFree(S.recv);
+  if (S.pads) (void)hipFree(S.pads);
+  if (S.words) (void)hipFree(S.words);
+  if (S.ctl) (void)hipHostFree(S.ctl);
+  if (S.flags) (void)hipHostFree(S.flags);
+  S.send = S.recv = nullptr;
+  S.pads = S.words = nullptr;
+  S.ctl = S.ctl_dev = nullptr;
+  S.flags = S.flags_dev = nullptr;
+}
+
+int init_impl(int world, size_t max_n, int rank) {
+  if (S.inited) return fail(ARX_ESTATE, "arx is already initialised in this process");
+  if (world < 2 || world > ARX_MAX_WORLD) return fail(ARX_EINVAL, "world %d not in [2, %d]", world, ARX_MAX_WORLD);
+  if (rank < 0 || rank >= world) return fail(ARX_EINVAL, "rank %d not in [0, %d)", rank, world);
+  if (max_n < 1 || max_n > ARX_MAX_N)
+    return fail(ARX_EINVAL, "max_n %zu not in [1, %zu]", max_n, (size_t)ARX_MAX_N);
+  S.world = world;
+  S.rank = rank;
+  S.max_n = max_n;
+  S.stride = (max_n + 127) & ~(size_t)127;
+  HIPCHK(hipGetDevice(&S.device));
+  int khz = 0;
+  HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, S.device));
+  S.clock_khz = khz > 0 ? (uint64_t)khz : 100000;
+
+  const size_t send_b = 2 * S.stride * sizeof(uint16_t);
+  const size_t recv_b = 2 * (size_t)world * S.stride * sizeof(uint16_t);
+  const size_t pads_b = (size_t)world * ARX_MAX_PAD_BLOCKS * world * sizeof(uint32_t);
+  const size_t words_b = arx::WORDS_TOTAL * sizeof(uint32_t);
+  int rc = ARX_OK;
+  hipError_t e;
+  if ((e = hipMalloc(&S.send, send_b)) != hipSuccess || (e = hipMalloc(&S.recv, recv_b)) != hipSuccess ||
+      (e = hipMalloc(&S.pads, pads_b)) != hipSuccess || (e = hipMalloc(&S.words, words_b)) != hipSuccess) {
+    rc = fail(ARX_ENOMEM, "device allocation of %zu bytes failed: %s", send_b + recv_b + pads_b + words_b,
+              hipGetErrorString(e));
+  } else if ((e = hipHostMalloc((void**)&S.ctl, 4096, hipHostMallocCoherent | hipHostMallocMapped)) !=
+                 hipSuccess ||
+             (e = hipHostMalloc((void**)&S.flags, 4096, hipHostMallocCoherent | hipHostMallocMapped)) !=
+                 hipSuccess) {
+    rc = fail(ARX_ENOMEM, "pinned allocation failed: %s", hipGetErrorString(e));
+  } else if ((e = hipMemset(S.send, 0, send_b)) != hipSuccess || (e = hipMemset(S.recv, 0, recv_b)) != hipSuccess ||
+             (e = hipMemset(S.pads, 0, pads_b)) != hipSuccess ||
+             (e = hipMemset(S.words, 0, words_b)) != hipSuccess ||
+             (e = hipHostGetDevicePointer((void**)&S.ctl_dev, S.ctl, 0)) != hipSuccess ||
+             (e = hipHostGetDevicePointer((void**)&S.flags_dev, S.flags, 0)) != hipSuccess ||
+             (e = hipDeviceSynchronize()) != hipSuccess) {
+    rc = fail(ARX_EHIP, "initialising device state failed: %s", hipGetErrorString(e));
+  }
+  if (rc != ARX_OK) {
+    free_all();
+    return rc;
+  }
+  memset((void*)S.ctl, 0, 4096);
+  memset((void*)S.flags, 0, 4096);
+  S.posted.store(0);
+  S.proxy_err.store(false);
+  S.stop.store(false);
+  S.stalls.store(0);
+  S.mode.store(ARX_PROXY_LOCKSTEP);
+  S.timeout_us = 2000000;
+  S.proxy = std::thread(proxy_loop);
+  S.inited = true;
+  return ARX_OK;
+}
+
+int check_ptrs(const void* in, const void* out, size_t n) {
+  if (n > S.max_n) return fail(ARX_EINVAL, "n %zu exceeds max_n %zu", n, S.max_n);
+  if (n > 0 && (in == nullptr || out == nullptr)) return fail(ARX_EINVAL, "null in or out");
+  if (((uintptr_t)in & 15u) || ((uintptr_t)out & 15u)) return fail(ARX_EINVAL, "in and out must be 16-byte aligned");
+  return ARX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int arx_init(int world, size_t max_n) { return init_impl(world, max_n, 0); }
+
+int arx_init_rank(int world, size_t max_n, int rank) { return init_impl(world, max_n, rank); }
+
+int arx_finalize(void) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  // let in-flight calls finish while the proxy still posts their flags
+  const hipError_t e = hipDeviceSynchronize();
+  S.stop.store(true, std::memory_order_release);
+  store_release(&S.ctl->stop, 1);
+  if (S.proxy.joinable()) S.proxy.join();
+  free_all();
+  S.inited = false;
+  S.world = S.rank = 0;
+  S.max_n = S.stride = 0;
+  if (e != hipSuccess) return fail(ARX_EHIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  return ARX_OK;
+}
+
+int arx_publish(uint64_t seq) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  std::lock_guard<std::mutex> g(S.publish_mu);
+  return publish_locked(seq);
+}
+
+int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream) {
+  int rc = check_ready();
+  if (rc != ARX_OK) return rc;
+  if ((rc = check_ptrs(in, out, n)) != ARX_OK) return rc;
+  arx::OneShotArgs a;
+  a.in = (const uint16_t*)in;
+  a.out = (uint16_t*)out;
+  a.send = S.send;
+  a.recv = S.recv;
+  a.stride = S.stride;
+  a.flags = S.flags_dev;
+  a.ctl = S.ctl_dev;
+  a.words = S.words;
+  a.n = (uint32_t)n;
+  a.rank = S.rank;
+  a.timeout = timeout_ticks();
+  HIPCHK(arx::launch_oneshot(a, S.world, stream));
+  return ARX_OK;
+}
+
+int arx_reduce(const void* in, void* out, size_t n, int par, hipStream_t stream) {
+  int rc = check_ready();
+  if (rc != ARX_OK) return rc;
+  if (par != 0 && par != 1) return fail(ARX_EINVAL, "par %d not in {0, 1}", par);
+  if ((rc = check_ptrs(in, out, n)) != ARX_OK) return rc;
+  if (n == 0) return ARX_OK;
+  arx::ReduceArgs a;
+  a.in = (const uint16_t*)in;
+  a.out = (uint16_t*)out;
+  a.recv_par = S.recv + (size_t)par * S.world * S.stride;
+  a.stride = S.stride;
+  a.n = (uint32_t)n;
+  a.rank = S.rank;
+  HIPCHK(arx::launch_reduce(a, S.world, stream));
+  return ARX_OK;
+}
+
+int arx_barrier_blockwise(int nblocks, int sem, int rounds, hipStream_t stream) {
+  int rc = check_ready();
+  if (rc != ARX_OK) return rc;
+  if (nblocks < 1 || nblocks > ARX_MAX_PAD_BLOCKS)
+    return fail(ARX_EINVAL, "nblocks %d not in [1, %d]", nblocks, ARX_MAX_PAD_BLOCKS);
+  if (sem != ARX_SEM_RELAXED && sem != ARX_SEM_ACQ_REL) return fail(ARX_EINVAL, "sem %d unknown", sem);
+  if (rounds < 1 || rounds > 64) return fail(ARX_EINVAL, "rounds %d not in [1, 64]", rounds);
+  arx::BarrierArgs a;
+  for (int i = 0; i < 8; ++i)
+    a.pad[i] = i < S.world ? S.pads + (size_t)i * ARX_MAX_PAD_BLOCKS * S.world : nullptr;
+  a.world = S.world;
+  a.acq_rel = sem == ARX_SEM_ACQ_REL;
+  a.rounds = rounds;
+  a.timeout = timeout_ticks();
+  a.ctl = S.ctl_dev;
+  HIPCHK(arx::launch_barrier(a, nblocks, stream));
+  return ARX_OK;
+}
+
+void* arx_recv_ptr(int par, int src) {
+  if (!S.inited || (par != 0 && par != 1) || src < 0 || src >= S.world) return nullptr;
+  return S.recv + ((size_t)par * S.world + src) * S.stride;
+}
+
+void* arx_send_ptr(int par) {
+  if (!S.inited || (par != 0 && par != 1)) return nullptr;
+  return S.send + (size_t)par * S.stride;
+}
+
+uint32_t* arx_pad_ptr(int rank) {
+  if (!S.inited || rank < 0 || rank >= S.world) return nullptr;
+  return S.pads + (size_t)rank * ARX_MAX_PAD_BLOCKS * S.world;
+}
+
+int arx_set_proxy_mode(int mode) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  if (mode != ARX_PROXY_LOCKSTEP && mode != ARX_PROXY_RUNAHEAD && mode != ARX_PROXY_MANUAL)
+    return fail(ARX_EINVAL, "proxy mode %d unknown", mode);
+  S.mode.store(mode);
+  return ARX_OK;
+}
+
+int arx_set_timeout_us(uint64_t us) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  if (us < 1 || us > 60000000ull) return fail(ARX_EINVAL, "timeout %llu us not in [1, 60000000]",
+                                              (unsigned long long)us);
+  S.timeout_us = us;
+  return ARX_OK;
+}
+
+int arx_status(uint64_t* published, uint64_t* posted, uint64_t* done) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  if (published) *published = load_acquire(&S.ctl->seq);
+  if (posted) *posted = S.posted.load();
+  if (done) *done = load_acquire(&S.ctl->done);
+  return ARX_OK;
+}
+
+int arx_debug_state(uint64_t* words, int nwords) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  if (words == nullptr || nwords < 0) return fail(ARX_EINVAL, "bad output array");
+  HIPCHK(hipDeviceSynchronize());
+  uint32_t dw[arx::WORDS_TOTAL];
+  HIPCHK(hipMemcpy(dw, S.words, sizeof dw, hipMemcpyDeviceToHost));
+  uint64_t all[12 + ARX_MAX_WORLD];
+  all[0] = dw[arx::WORD_SEQ];
+  all[1] = dw[arx::WORD_CNT0];
+  all[2] = dw[arx::WORD_CNT1];
+  all[3] = dw[arx::WORD_GO];
+  all[4] = dw[arx::WORD_ABORT];
+  all[5] = load_acquire(&S.ctl->seq);
+  all[6] = load_acquire(&S.ctl->bytes[0]);
+  all[7] = load_acquire(&S.ctl->bytes[1]);
+  all[8] = load_acquire(&S.ctl->done);
+  all[9] = load_acquire(&S.ctl->err);
+  all[10] = load_acquire(&S.ctl->err_seq);
+  all[11] = S.posted.load();
+  for (int i = 0; i < S.world; ++i) all[12 + i] = load_acquire(&S.flags[i]);
+  const int total = 12 + S.world;
+  const int m = nwords < total ? nwords : total;
+  for (int i = 0; i < m; ++i) words[i] = all[i];
+  return m;
+}
+
+int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream) {
+  if (n > 0xFFFFFFFFull) return fail(ARX_EINVAL, "n %zu too large", n);
+  if (n > 0 && (in == nullptr || out == nullptr)) return fail(ARX_EINVAL, "null in or out");
+  if (n == 0) return ARX_OK;
+  HIPCHK(arx::launch_round_test((const uint32_t*)in, (uint16_t*)out, n, stream));
+  return ARX_OK;
+}
+
+const char* arx_strerror(int err) {
+  static char buf[640];
+  const char* base;
+  switch (err) {
+    case ARX_OK: return "ok";
+    case ARX_EINVAL: base = "invalid argument"; break;
+    case ARX_ESTATE: base = "wrong library state"; break;
+    case ARX_ENOMEM: base = "out of memory"; break;
+    case ARX_EHIP: base = "HIP error"; break;
+    case ARX_EPROXY: base = "proxy thread failed"; break;
+    case ARX_EORDER: base = "seq published out of order"; break;
+    case ARX_ETIMEOUT: base = "device wait timed out"; break;
+    default: return "unknown error";
+  }
+  if (g_detail[0]) snprintf(buf, sizeof buf, "%s: %s", base, g_detail);
+  else snprintf(buf, sizeof buf, "%s", base);
+  return buf;
+}
+
+size_t arx_max_n(void) { return S.inited ? S.max_n : 0; }
+int arx_world(void) { return S.inited ? S.world : 0; }
+int arx_rank(void) { return S.inited ? S.rank : 0; }
+
+}  // extern "C"

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, bit-exact.
+
+Every output element is compared with the oracle's (0 ulp, NaN patterns
+included), elements past n are checked untouched, and every protocol word is
+read back and compared with the oracle's sequential protocol model.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import protocol as P
+from oracle import reduce as R
+from signal_pad_sync_amd import arx
+from signal_pad_sync_amd import workloads as WL
+from tests.gpu_util import fill_recv, library, note, sentinel, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def assert_bits(got, want, what):
+    if not np.array_equal(got, want):
+        bad = np.flatnonzero(got != want)
+        i = int(bad[0])
+        raise AssertionError(f"{what}: {bad.size} elements differ, first at {i}: "
+                             f"got {hex(int(got[i]))} want {hex(int(want[i]))}")
+
+
+def check_state(st: P.ProtocolState, rank: int, wait_posted: int = None):
+    """Compares every protocol word with the model's prediction."""
+    if wait_posted is not None:       # the proxy posts asynchronously in run-ahead mode
+        t0 = time.time()
+        while arx.status()[1] < wait_posted and time.time() - t0 < 5:
+            time.sleep(0.001)
+    d = arx.debug_state()
+    assert d["ctl_err"] == 0, d
+    assert d["cnt0"] == 0 and d["cnt1"] == 0, d
+    assert d["seq_dev"] == st.seq_dev and d["go"] == st.go, d
+    assert d["ctl_seq"] == st.ctl_seq and d["ctl_done"] == st.ctl_done, d
+    assert [d["ctl_bytes0"], d["ctl_bytes1"]] == st.ctl_bytes, d
+    assert d["posted"] == st.posted, d
+    assert d["flags"] == st.flags, (d["flags"], st.flags)
+
+
+def test_round_bf16_exhaustive():
+    """The device rounding equals the oracle's on all 2^32 binary32 patterns."""
+    chunk = 1 << 26
+    base = torch.arange(chunk, dtype=torch.int32, device="cuda")
+    out = torch.empty(chunk, dtype=torch.int16, device="cuda")
+    for k in range((1 << 32) // chunk):
+        start = k * chunk
+        if k % 16 == 0:
+            note(f"round_bf16 chunk {k}")
+        inp = base + (start if start < (1 << 31) else start - (1 << 32))
+        arx.test_round_bf16(inp, out)
+        got = out.cpu().numpy().view(np.uint16)
+        want = R.round_bf16(np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32))
+        assert_bits(got, want, f"rounding chunk at {hex(start)}")
+
+
+def test_workload1_single_call():
+    """W=2, [2, 4096], N(0,1); one call, seq 1, parity 1."""
+    W, n = 2, 8192
+    recv = [WL.recv_partials(1, par, n) for par in (0, 1)]
+    x = recv[1][0]
+    with library(W, n):
+        fill_recv(recv, 0)
+        inp, out = to_dev(x), sentinel(n + 64)
+        note("workload 1 allreduce")
+        arx.allreduce(inp, out, n)
+        torch.cuda.synchronize()
+        got = to_host(out)
+        st, outs = P.sequential_model([(x, n)], recv, W)
+        assert_bits(got[:n], outs[0], "workload 1")
+        assert np.all(got[n:] == 0xDEAD)
+        check_state(st, 0)
+        assert_bits(to_host(arx.send_view(1, n)), x, "send slot 1")
+
+
+@pytest.mark.parametrize("mode,K", [(arx.PROXY_LOCKSTEP, 1000), (arx.PROXY_RUNAHEAD, 300)])
+def test_workload2_consecutive_calls(mode, K):
+    """W=8, [32, 4096], N(0,1)*0.1; K consecutive calls with a fresh partial
+    each, parity alternating, flags posted by the proxy thread."""
+    W, n = 8, 131072
+    recv = [WL.recv_partials(2, par, n) for par in (0, 1)]
+    ins = np.stack([WL.own_partial(2, k, n) for k in range(1, K + 1)])
+    with library(W, n, mode=mode):
+        fill_recv(recv, 0)
+        din = to_dev(ins.reshape(-1)).view(K, n)
+        dout = torch.empty_like(din)
+        note(f"workload 2: {K} calls, mode {mode}")
+        for k in range(K):
+            arx.allreduce(din[k], dout[k], n)
+        torch.cuda.synchronize()
+        got = to_host(dout).reshape(K, n)
+        st, outs = P.sequential_model([(ins[k], n) for k in range(K)], recv, W,
+                                      mode=P.RUNAHEAD if mode == arx.PROXY_RUNAHEAD else P.LOCKSTEP)
+        for k in range(K):
+            assert_bits(got[k], outs[k], f"workload 2 call {k + 1}")
+        check_state(st, 0, wait_posted=st.posted)
+        assert_bits(to_host(arx.send_view(K & 1, n)), ins[K - 1], "send slot of the last call")
+        assert_bits(to_host(arx.send_view((K - 1) & 1, n)), ins[K - 2], "send slot of the call before")
+
+
+@pytest.mark.parametrize("n", WL.WORKLOADS[3]["ns"])
+def test_workload3_graph_with_barrier(n):
+    """W=4, uniform[-1,1]; the one-shot call and a 256-workgroup blockwise
+    barrier captured in one hipGraph, replayed with eager calls between the
+    replays; every replay matches the oracle and leaves every pad zero."""
+    W = 4
+    recv = [WL.recv_partials(3, par, n) for par in (0, 1)]
+    x = WL.own_partial(3, 1, n)
+    y = WL.own_partial(3, 2, n)
+    with library(W, n):
+        fill_recv(recv, 0)
+        inp, out = to_dev(x), sentinel(n + 16)
+        inp2, out2 = to_dev(y), sentinel(n + 16)
+        g = torch.cuda.CUDAGraph()
+        note(f"workload 3 n={n}: capture")
+        with torch.cuda.graph(g):
+            arx.allreduce(inp, out, n)
+            arx.barrier_blockwise(256, arx.SEM_ACQ_REL, 1)
+        st = None
+        for rep in range(6):
+            note(f"workload 3 n={n}: replay {rep}")
+            g.replay()
+            torch.cuda.synchronize()
+            st, outs = P.sequential_model([(x, n)], recv, W, state=st)
+            got = to_host(out)
+            assert_bits(got[:n], outs[0], f"replay {rep}")
+            assert np.all(got[n:] == 0xDEAD)
+            for r in range(W):
+                assert int(arx.pad_view(r).abs().sum()) == 0, f"pad {r} not zero after replay {rep}"
+            check_state(st, 0)
+            if rep in (1, 2):             # eager work between replays
+                arx.allreduce(inp2, out2, n)
+                torch.cuda.synchronize()
+                st, outs = P.sequential_model([(y, n)], recv, W, state=st)
+                assert_bits(to_host(out2)[:n], outs[0], f"eager call after replay {rep}")
+
+
+def test_workload4_reduce_full_size():
+    """W=8, [8192, 8192] (128 MiB per partial), N(0,1); reduction alone."""
+    W, n = 8, 8192 * 8192
+    note("workload 4: generating inputs")
+    parts = WL.recv_partials(4, 0, n)
+    with library(W, n):
+        fill_recv([parts, None], 0)
+        inp = to_dev(parts[0])
+        out = torch.empty_like(inp)
+        note("workload 4: reduce")
+        arx.reduce(inp, out, 0, n)
+        torch.cuda.synchronize()
+        got = to_host(out)
+        assert_bits(got, R.reduce(parts, threads=16), "workload 4")
+
+
+def test_workload5_adversarial():
+    """W=8, [32, 4096] buffers, n = 131071, adversarial values: one-shot call
+    and the reduction alone, both bit-exact, out[131071] untouched."""
+    W, n, buf = 8, 131071, 131072
+    recv = [WL.recv_partials(5, par, n) for par in (0, 1)]
+    x = recv[1][0]
+    with library(W, buf):
+        fill_recv(recv, 0)
+        inp, out = to_dev(x, pad_to=buf), sentinel(buf)
+        note("workload 5 allreduce")
+        arx.allreduce(inp, out, n)
+        torch.cuda.synchronize()
+        st, outs = P.sequential_model([(x, n)], recv, W, max_n=buf)
+        got = to_host(out)
+        assert_bits(got[:n], outs[0], "workload 5 one-shot")
+        assert got[n] == 0xDEAD
+        check_state(st, 0)
+        out2 = sentinel(buf)
+        note("workload 5 reduce")
+        arx.reduce(inp, out2, 0, n)
+        torch.cuda.synchronize()
+        got2 = to_host(out2)
+        assert_bits(got2[:n], R.reduce([x] + recv[0][1:], n=n), "workload 5 reduce only")
+        assert got2[n] == 0xDEAD
+
+
+@pytest.mark.parametrize("W,rank", [(3, 1), (5, 4), (8, 3)])
+def test_sizes_tails_and_rank(W, rank):
+    """Any n (tails of 1..7, partial workgroups, n = 0), this GPU at rank r,
+    one call after another; includes n past one pass of the co-resident grid."""
+    max_n = (1 << 20) + 64
+    sizes = [0, 1, 7, 8, 9, 15, 17, 255, 256, 257, 1000, 2047, 2049, 65539, 524288, 524289, 1 << 20]
+    rng = np.random.default_rng(7 + W)
+    recv = [[WL.uniform(9000 + 10 * par + s, max_n) for s in range(W)] for par in (0, 1)]
+    with library(W, max_n, rank=rank):
+        fill_recv(recv, rank)
+        st = None
+        for n in sizes:
+            x = WL.uniform(int(rng.integers(1 << 30)), max(n, 1))[:n]
+            inp, out = to_dev(x, pad_to=max_n), sentinel(max_n)
+            note(f"W={W} rank={rank} n={n}")
+            arx.allreduce(inp, out, n)
+            torch.cuda.synchronize()
+            st, outs = P.sequential_model([(x, n)], recv, W, rank=rank, max_n=max_n, state=st)
+            got = to_host(out)
+            assert_bits(got[:n], outs[0], f"W={W} rank={rank} n={n}")
+            assert np.all(got[n:] == 0xDEAD), n
+        check_state(st, rank)
+
+
+def test_in_place():
+    """in and out may be the same buffer."""
+    W, n = 4, 100003
+    recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
+    x = WL.own_partial(3, 7, n)
+    with library(W, n + 5):
+        fill_recv(recv, 0)
+        buf = to_dev(x, pad_to=n + 5)
+        note("in-place allreduce")
+        arx.allreduce(buf, buf, n)
+        torch.cuda.synchronize()
+        _, outs = P.sequential_model([(x, n)], recv, W, max_n=n + 5)
+        assert_bits(to_host(buf)[:n], outs[0], "in place")
+
+
+def test_manual_publish_and_order():
+    """Manual mode: the kernel waits until the caller publishes; a publish
+    out of order is refused and writes nothing."""
+    W, n = 4, 4096
+    recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
+    x = WL.own_partial(3, 9, n)
+    with library(W, n, mode=arx.PROXY_MANUAL):
+        fill_recv(recv, 0)
+        inp, out = to_dev(x), sentinel(n)
+        note("manual publish")
+        arx.allreduce(inp, out, n)
+        with pytest.raises(arx.ArxError) as e:
+            arx.publish(2)
+        assert e.value.code == arx.EORDER
+        arx.publish(1)
+        torch.cuda.synchronize()
+        st, outs = P.sequential_model([(x, n)], recv, W, mode=P.MANUAL,
+                                      state=P.ProtocolState(W=W, rank=0, flags=[0, 1, 1, 1], posted=1))
+        assert_bits(to_host(out), outs[0], "manual")
+        check_state(st, 0)
+
+
+def test_flag_timeout_is_latched():
+    """No flag ever comes (manual mode, never published): the bounded wait
+    runs out, the output stays untouched, counters still reset, seq advances,
+    and the next call reports the timeout."""
+    W, n = 2, 4096
+    with library(W, n, mode=arx.PROXY_MANUAL, timeout_us=20000):
+        inp, out = to_dev(np.ones(n, np.uint16)), sentinel(n)
+        note("forced flag timeout (20 ms)")
+        arx.allreduce(inp, out, n)
+        torch.cuda.synchronize()
+        assert np.all(to_host(out) == 0xDEAD)
+        d = arx.debug_state()
+        assert d["ctl_err"] == 1 and d["ctl_err_seq"] == 1 and d["abort"] == 1
+        assert d["cnt0"] == 0 and d["cnt1"] == 0 and d["seq_dev"] == 1 and d["ctl_done"] == 1
+        with pytest.raises(arx.ArxError) as e:
+            arx.allreduce(inp, out, n)
+        assert e.value.code == arx.ETIMEOUT
+
+
+def test_argument_errors():
+    with library(2, 1024):
+        t = torch.zeros(2048, dtype=torch.bfloat16, device="cuda")
+        for call in (lambda: arx.allreduce(t, t, 1025), lambda: arx.allreduce(t[1:], t, 8),
+                     lambda: arx.reduce(t, t, 2, 8), lambda: arx.barrier_blockwise(1025),
+                     lambda: arx.barrier_blockwise(4, 7), lambda: arx.set_proxy_mode(5),
+                     lambda: arx.set_timeout_us(0)):
+            with pytest.raises(arx.ArxError) as e:
+                call()
+            assert e.value.code == arx.EINVAL
+        with pytest.raises(arx.ArxError) as e:
+            arx.init(2, 16)
+        assert e.value.code == arx.ESTATE
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_barrier_leaves_pads_zero(W):
+    """Page "triton_barrier.py": the pad is zero-filled again after every
+    barrier; many workgroups, both semantics, repeated rounds."""
+    with library(W, 1024):
+        for sem in (arx.SEM_RELAXED, arx.SEM_ACQ_REL):
+            for nblocks, rounds in [(1, 1), (32, 1), (256, 1), (256, 8), (1024, 2), (1024, 64)]:
+                note(f"barrier W={W} sem={sem} nblocks={nblocks} rounds={rounds}")
+                arx.barrier_blockwise(nblocks, sem, rounds)
+                torch.cuda.synchronize()
+                for r in range(W):
+                    assert int(arx.pad_view(r).abs().sum()) == 0
+                assert arx.debug_state()["ctl_err"] == 0
