@@ -43,8 +43,11 @@ template <typename T>
 __device__ __forceinline__ void store_release_system(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
-__device__ __forceinline__ uint32_t fetch_add_acq_rel_agent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t fetch_add_release_system(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint32_t fetch_add_relaxed_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void fence_acquire_system() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, ""); }
@@ -152,28 +155,34 @@ struct Pads {
 // calling group (rank `rank`, block id `block_id`) signals rank `lane` by a
 // CAS 0 -> 1 on slot (block_id, rank) of that rank's pad, retried while the
 // slot still holds an unconsumed 1, then consumes rank `lane`'s signal by a
-// CAS 1 -> 0 on slot (block_id, lane) of its own pad. With acq_rel the
-// signal is a release and the consume an acquire; relaxed uses neither.
-// Every successful barrier leaves the slots it used at zero. Each wait gives
-// up after `timeout` wall-clock ticks; returns false if one did. Lanes >=
-// world return true at once. The caller adds the workgroup barriers that a
-// usage pattern needs (before for publishing, after for acquiring).
+// CAS 1 -> 0 on slot (block_id, lane) of its own pad. With acq_rel the signal
+// is a release and the consume an acquire; relaxed uses neither. The CASes
+// themselves are relaxed and the release / acquire are fences placed before
+// the first signal attempt and after the successful consume, which orders
+// the same accesses as a release CAS and an acquire CAS while keeping the
+// cache write-back and invalidate out of the retry loops. Every successful
+// barrier leaves the slots it used at zero. Each wait gives up after
+// `timeout` wall-clock ticks; returns false if one did. Lanes >= world
+// return true at once. The caller adds the workgroup barriers that a usage
+// pattern needs (before for publishing, after for acquiring).
 __device__ __forceinline__ bool barrier_blockwise(const Pads& p, uint32_t block_id, int rank, int lane,
                                                   bool acq_rel, uint64_t timeout) {
   if (lane >= p.world) return true;
   const int W = p.world;
   uint32_t* send = p.pad[lane] + (size_t)block_id * W + rank;
   uint32_t* wait = p.pad[rank] + (size_t)block_id * W + lane;
+  if (acq_rel) fence_release_system();
   const uint64_t t0 = now_ticks();
-  while (!cas_system(send, 0u, 1u, acq_rel ? __ATOMIC_RELEASE : __ATOMIC_RELAXED)) {
+  while (!cas_system(send, 0u, 1u, __ATOMIC_RELAXED)) {
     if (now_ticks() - t0 > timeout) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   const uint64_t t1 = now_ticks();
-  while (!cas_system(wait, 1u, 0u, acq_rel ? __ATOMIC_ACQUIRE : __ATOMIC_RELAXED)) {
+  while (!cas_system(wait, 1u, 0u, __ATOMIC_RELAXED)) {
     if (now_ticks() - t1 > timeout) return false;
     __builtin_amdgcn_s_sleep(1);
   }
+  if (acq_rel) fence_acquire_system();
   return true;
 }
 

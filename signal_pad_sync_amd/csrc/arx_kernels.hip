@@ -88,14 +88,15 @@ __global__ __launch_bounds__(kBlock) void oneshot_kernel(OneShotArgs a) {
     for (uint32_t v = tid; v < nv; v += nthr) st16(mine + 8u * (size_t)v, ld16(a.in + 8u * (size_t)v));
   }
   if (tid < tail) mine[8u * (size_t)nv + tid] = a.in[8u * (size_t)nv + tid];
-  // every wave's copy is complete and written back before its workgroup counts in
-  fence_release_system();
   __syncthreads();
 
-  // 2. arrival count; the last workgroup to arrive resets the counter and
+  // 2. arrival count: one system-scope release per workgroup carries all its
+  //    waves' copies (they precede it through the workgroup barrier); the
+  //    last workgroup to arrive acquires them all, resets the counter and
   //    publishes seq to the host proxy
   if (threadIdx.x == 0) {
-    if (fetch_add_acq_rel_agent(cnt0, 1u) == gridDim.x - 1u) {
+    if (fetch_add_release_system(cnt0, 1u) == gridDim.x - 1u) {
+      fence_acquire_system();
       store_relaxed_agent(cnt0, 0u);
       store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
       store_release_system(&a.ctl->seq, (uint64_t)seq);
@@ -180,13 +181,16 @@ __global__ __launch_bounds__(kBlock) void oneshot_kernel(OneShotArgs a) {
     }
   }
 
-  // 5. last block out: reset the finish counter, record the completed seq
+  // 5. last block out: reset the finish counter, record the completed seq.
+  //    Relaxed: the only reader of the counter and of seq_dev is the next
+  //    kernel on the stream, which the kernel boundary already orders after
+  //    this one; ctl.done is progress information for the host.
   __syncthreads();
   if (threadIdx.x == 0) {
-    if (fetch_add_acq_rel_agent(cnt1, 1u) == gridDim.x - 1u) {
+    if (fetch_add_relaxed_agent(cnt1, 1u) == gridDim.x - 1u) {
       store_relaxed_agent(cnt1, 0u);
       store_relaxed_agent(seq_dev, seq);
-      store_release_system(&a.ctl->done, (uint64_t)seq);
+      store_relaxed_system(&a.ctl->done, (uint64_t)seq);
     }
   }
 }
