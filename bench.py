@@ -29,6 +29,22 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "one-shot reduce GB/s (% of HBM peak) + µs/call at W=8, 256 KB bf16"
 
 
+def recorded_traffic(key):
+    """HBM bytes per launch measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs summarised in profiles/hbm_traffic_pmc.md, or None when the kernel
+    sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in ("arx_kernels.hip", "arx_device.h", "arx_internal.h"):
+        with open(os.path.join(ROOT, "signal_pad_sync_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return rec.get(key) if rec.get("kernel_source_sha256") == h.hexdigest() else None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -41,7 +57,7 @@ def parse():
     ap.add_argument("--reduce-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of phases: oneshot,runahead,graph,reduce,barrier")
+    ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,graph,reduce,barrier")
     return ap.parse_args()
 
 
@@ -83,12 +99,18 @@ def bench_oneshot(args, mode, graph=False):
                     arx.allreduce(x, out, n)
             fn, reps = g.replay, max(1, args.steps // per)
         else:
+            # the timed loop calls the C entry point directly with its
+            # arguments prepared once, so Python adds as little as possible
             per = 1
-            fn, reps = (lambda: arx.allreduce(x, out, n)), args.steps
+            call, xp, op, sh = arx.lib.arx_allreduce, x.data_ptr(), out.data_ptr(), stream.cuda_stream
+            rcs = []
+            fn, reps = (lambda: rcs.append(call(xp, op, n, sh))), args.steps
         for _ in range(max(1, args.warmup // per)):
             fn()
         us = timed(fn, reps, stream)
         calls = reps * per
+        if not graph:
+            assert not any(rcs), f"arx_allreduce failed: {set(rcs)}"
         st = arx.debug_state()
         assert st["ctl_err"] == 0 and st["cnt0"] == 0 and st["cnt1"] == 0, st
     finally:
@@ -131,22 +153,45 @@ def bench_reduce(args):
     return samples[len(samples) // 2], us_total / args.reduce_reps
 
 
-def bench_barrier(args):
+def bench_barrier(args, sem):
+    """256-workgroup blockwise barrier at W=8, 100 launches per hipGraph;
+    returns microseconds per launch."""
     import torch
     from signal_pad_sync_amd import arx
     arx.init(8, 1024)
     try:
         stream = torch.cuda.current_stream()
-        fn = lambda: arx.barrier_blockwise(256, arx.SEM_ACQ_REL, 1)
-        for _ in range(args.warmup):
-            fn()
-        us = timed(fn, args.steps, stream)
+        per = 100
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per):
+                arx.barrier_blockwise(256, sem, 1)
+        for _ in range(3):
+            g.replay()
+        reps = max(1, args.steps // per)
+        us = timed(g.replay, reps, stream)
         for r in range(8):
             assert int(arx.pad_view(r).abs().sum()) == 0
+        assert arx.debug_state()["ctl_err"] == 0
     finally:
         torch.cuda.synchronize()
         arx.finalize()
-    return us / args.steps
+    return us / (reps * per)
+
+
+def bench_copy(args):
+    """A plain device-to-device copy of 64 MiB: the achievable-bandwidth
+    reference, and the known-size kernel that scales the HBM byte counters."""
+    import torch
+    n = 32 << 20
+    a = torch.randn(n, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        b.copy_(a)
+    reps = 20
+    us = timed(lambda: b.copy_(a), reps, stream) / reps
+    return 2 * n * 2, us
 
 
 def cpu_baseline(seconds):
@@ -186,6 +231,11 @@ def main():
     extra = {}
 
     us_call = None
+    if want("copy"):
+        log("plain device copy, 64 MiB")
+        cb, cus = bench_copy(args)
+        extra["copy_64MiB"] = {"bytes_per_call": cb, "us": round(cus, 2), "GBps": round(cb / cus / 1e3, 1)}
+        log(f"  {cus:.1f} us, {cb / cus / 1e3:.0f} GB/s (read + write)")
     if want("oneshot"):
         log("one-shot, lockstep proxy")
         us_call, calls = bench_oneshot(args, arx.PROXY_LOCKSTEP)
@@ -207,12 +257,15 @@ def main():
         extra["reduce_128MiB"] = {
             "workload": "W=8, bf16 [8192,8192] per partial, reduction alone",
             "bytes_per_call": rb, "us_median": round(med, 2), "us_mean_back_to_back": round(mean, 2),
-            "GBps": round(rb / med / 1e3, 1), "frac_of_hbm_peak": round(rb / med / 1e3 / HBM_PEAK_GBS, 4)}
+            "GBps": round(rb / med / 1e3, 1), "frac_of_hbm_peak": round(rb / med / 1e3 / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("reduce_kernel_w8_n67108864_bytes")}
         log(f"  {med:.1f} us median, {rb / med / 1e3:.0f} GB/s")
     if want("barrier"):
-        log("blockwise barrier, 256 workgroups, W=8, acq_rel")
-        extra["barrier_256wg_us"] = round(bench_barrier(args), 3)
-        log(f"  {extra['barrier_256wg_us']} us/launch")
+        for name, sem in (("acq_rel", arx.SEM_ACQ_REL), ("relaxed", arx.SEM_RELAXED)):
+            log(f"blockwise barrier, 256 workgroups, W=8, {name}, 100 launches per hipGraph")
+            us_b = bench_barrier(args, sem)
+            extra[f"barrier_256wg_{name}_us"] = round(us_b, 3)
+            log(f"  {us_b:.3f} us/launch")
 
     cpu = None
     if not args.skip_cpu:
@@ -224,6 +277,9 @@ def main():
         log(f"  {cpu['us_per_call']} us/call on 1 core")
 
     value = bytes_call / us_call / 1e3 if us_call else None
+    # launches run back to back, so the event time of the timed region over
+    # the number of launches is the kernel's average launch duration
+    achieved = value
     line = {
         "metric": METRIC, "value": round(value, 2) if value else None, "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -234,9 +290,11 @@ def main():
                                "parity alternating, lockstep host-proxy flags in pinned memory",
                    "W": W, "n": n, "io_dtype": "bf16", "accumulate": "f32"},
         "us_per_call": round(us_call, 3) if us_call else None,
-        "roofline": {"bound": "hbm", "achieved": round(value, 2) if value else None, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 5) if value else None,
-                     "traffic": None, "kernel": "oneshot_kernel<8,true>", "bytes_per_launch": bytes_call},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
+                     "traffic": recorded_traffic("oneshot_kernel_w8_n131072_bytes"),
+                     "kernel": "oneshot_kernel<8,true>", "bytes_per_launch": bytes_call,
+                     "kernel_us": round(us_call, 3) if us_call else None},
         "cpu_baseline": cpu,
         "extra": extra,
     }

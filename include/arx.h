@@ -129,9 +129,10 @@ int arx_reduce(const void* in, void* out, size_t n, int par, hipStream_t stream)
 /*
  * arx_barrier_blockwise — launch `nblocks` workgroups; workgroup b runs the
  * blockwise signal-pad barrier on block id b for all W virtual ranks (page
- * "triton_barrier.py": blockwise_barrier, send_signal, wait_signal): wave v
- * plays rank v, its lane s < W CASes slot v of block b in rank s's pad from
- * 0 to 1 and then CASes slot s of block b in its own pad from 1 to 0. The
+ * "triton_barrier.py": blockwise_barrier, send_signal, wait_signal): in the
+ * workgroup's single wave, lanes [v*W, v*W + W) play rank v, and its lane s
+ * CASes slot v of block b in rank s's pad from 0 to 1 and then CASes slot s
+ * of block b in its own pad from 1 to 0. The
  * pads start zero-filled and are zero-filled again after every barrier, so
  * the launch is hipGraph-capturable with no host reset.
  *   nblocks: 1..ARX_MAX_PAD_BLOCKS.  sem: ARX_SEM_RELAXED or ARX_SEM_ACQ_REL.

@@ -151,39 +151,56 @@ struct Pads {
   int world;
 };
 
-// Page "triton_barrier.py", blockwise_barrier: lane `lane` < world of the
-// calling group (rank `rank`, block id `block_id`) signals rank `lane` by a
-// CAS 0 -> 1 on slot (block_id, rank) of that rank's pad, retried while the
-// slot still holds an unconsumed 1, then consumes rank `lane`'s signal by a
-// CAS 1 -> 0 on slot (block_id, lane) of its own pad. With acq_rel the signal
-// is a release and the consume an acquire; relaxed uses neither. The CASes
-// themselves are relaxed and the release / acquire are fences placed before
-// the first signal attempt and after the successful consume, which orders
-// the same accesses as a release CAS and an acquire CAS while keeping the
-// cache write-back and invalidate out of the retry loops. Every successful
-// barrier leaves the slots it used at zero. Each wait gives up after
-// `timeout` wall-clock ticks; returns false if one did. Lanes >= world
-// return true at once. The caller adds the workgroup barriers that a usage
-// pattern needs (before for publishing, after for acquiring).
-__device__ __forceinline__ bool barrier_blockwise(const Pads& p, uint32_t block_id, int rank, int lane,
-                                                  bool acq_rel, uint64_t timeout) {
-  if (lane >= p.world) return true;
-  const int W = p.world;
-  uint32_t* send = p.pad[lane] + (size_t)block_id * W + rank;
-  uint32_t* wait = p.pad[rank] + (size_t)block_id * W + lane;
+// One lane's part of the barrier, on its two slots: signal by a CAS 0 -> 1
+// on `send_slot` (retried while the slot still holds an unconsumed 1), then
+// consume by a CAS 1 -> 0 on `wait_slot`. With acq_rel the signal is a
+// release and the consume an acquire; relaxed uses neither. The CASes are
+// relaxed and the release / acquire are fences placed before the first
+// signal attempt and after the successful consume, which orders the same
+// accesses as a release CAS and an acquire CAS while keeping the cache
+// write-back and invalidate out of the retry loops. Each wait gives up after
+// `timeout` wall-clock ticks; returns false if one did.
+__device__ __forceinline__ bool barrier_signal_wait(uint32_t* send_slot, uint32_t* wait_slot, bool acq_rel,
+                                                    uint64_t timeout) {
   if (acq_rel) fence_release_system();
   const uint64_t t0 = now_ticks();
-  while (!cas_system(send, 0u, 1u, __ATOMIC_RELAXED)) {
+  while (!cas_system(send_slot, 0u, 1u, __ATOMIC_RELAXED)) {
     if (now_ticks() - t0 > timeout) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   const uint64_t t1 = now_ticks();
-  while (!cas_system(wait, 1u, 0u, __ATOMIC_RELAXED)) {
+  while (!cas_system(wait_slot, 1u, 0u, __ATOMIC_RELAXED)) {
     if (now_ticks() - t1 > timeout) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   if (acq_rel) fence_acquire_system();
   return true;
+}
+
+// Element i of an array of 8 pointers for a per-lane i, picked by selects:
+// indexing the array with a per-lane value would move it to memory and turn
+// the CASes into slower generic-address atomics.
+__device__ __forceinline__ uint32_t* select_pad(uint32_t* const (&pad)[8], int i) {
+  uint32_t* r = pad[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) r = (i == k) ? pad[k] : r;
+  return r;
+}
+
+// Page "triton_barrier.py", blockwise_barrier: lane `lane` < world of the
+// calling group (rank `rank`, block id `block_id`) signals rank `lane` on
+// slot (block_id, rank) of that rank's pad, then consumes rank `lane`'s
+// signal on slot (block_id, lane) of its own pad (barrier_signal_wait gives
+// the CAS and ordering rules). Every successful barrier leaves the slots it
+// used at zero. Lanes >= world return true at once. The caller adds the
+// workgroup barriers that a usage pattern needs (before for publishing,
+// after for acquiring).
+__device__ __forceinline__ bool barrier_blockwise(const Pads& p, uint32_t block_id, int rank, int lane,
+                                                  bool acq_rel, uint64_t timeout) {
+  if (lane >= p.world) return true;
+  const size_t row = (size_t)block_id * p.world;
+  return barrier_signal_wait(select_pad(p.pad, lane) + row + rank, select_pad(p.pad, rank) + row + lane, acq_rel,
+                             timeout);
 }
 
 }  // namespace arx
