@@ -218,7 +218,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the one-shot reduction; the virtual peers live on the "
-              "same GPU, so --gpus must be 1 (no multi-GPU run exists in this build)", file=sys.stderr)
+              "same GPU, so --gpus must be 1 (there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
     from signal_pad_sync_amd import arx
