@@ -13,14 +13,20 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <memory>
 #include <thread>
 
 #include "arx.h"
 #include "arx_internal.h"
+#include "arx_proxy.h"
 
 namespace {
 
 using arx::Ctl;
+
+static_assert(ARX_PROXY_LOCKSTEP == arx::PROXY_LOCKSTEP && ARX_PROXY_RUNAHEAD == arx::PROXY_RUNAHEAD &&
+                  ARX_PROXY_MANUAL == arx::PROXY_MANUAL,
+              "proxy mode numbering");
 
 struct State {
   bool inited = false;
@@ -36,13 +42,10 @@ struct State {
   uint64_t* flags_dev = nullptr;
   uint64_t clock_khz = 100000;
   uint64_t timeout_us = 2000000;
+  std::unique_ptr<arx::Proxy> core;  // flag posting and the stall watchdog
   std::thread proxy;
-  std::atomic<int> mode{ARX_PROXY_LOCKSTEP};
-  std::atomic<uint64_t> posted{0};
   std::atomic<bool> proxy_err{false};
   std::atomic<bool> stop{false};
-  std::atomic<uint64_t> stalls{0};
-  std::mutex publish_mu;
 
   // A process that never called arx_finalize still must not end with a
   // joinable thread (that aborts): stop and join the proxy, CPU-side only.
@@ -74,66 +77,13 @@ int fail(int code, const char* fmt, ...) {
 inline uint64_t load_acquire(const uint64_t* p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
 inline void store_release(uint64_t* p, uint64_t v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
 
-// The virtual peers publish seq s: every flag but this rank's becomes s.
-int publish_locked(uint64_t s) {
-  const uint64_t last = S.posted.load(std::memory_order_acquire);
-  if (s != last + 1) return fail(ARX_EORDER, "arx_publish(%llu) after %llu: seqs are posted in order",
-                                 (unsigned long long)s, (unsigned long long)last);
-  for (int src = 0; src < S.world; ++src)
-    if (src != S.rank) store_release(&S.flags[src], s);
-  S.posted.store(s, std::memory_order_release);
-  return ARX_OK;
-}
-
-inline void cpu_relax() { __builtin_ia32_pause(); }
-
-// Proxy thread (page "arx.cu", proxy_loop): polls the seq this GPU published
-// and, in the lockstep and run-ahead modes, posts every seq in order up to
-// the target the mode allows. Between posts it acts as the watchdog: work
-// published but not finished for 2 s is reported once, with the peer flags.
-void proxy_loop() {
-  using clk = std::chrono::steady_clock;
-  uint64_t last_done = 0;
-  auto last_move = clk::now();
-  bool reported = false;
-  unsigned spin = 0;
-  while (!S.stop.load(std::memory_order_acquire)) {
-    const uint64_t pub = load_acquire(&S.ctl->seq);
-    const int mode = S.mode.load(std::memory_order_relaxed);
-    const uint64_t posted = S.posted.load(std::memory_order_acquire);
-    uint64_t target = posted;
-    if (mode == ARX_PROXY_LOCKSTEP) target = pub;
-    else if (mode == ARX_PROXY_RUNAHEAD) target = pub + 1;
-    if (target > posted) {
-      std::lock_guard<std::mutex> g(S.publish_mu);
-      for (uint64_t s = S.posted.load() + 1; s <= target; ++s)
-        if (publish_locked(s) != ARX_OK) {
-          fprintf(stderr, "arx rank %d: proxy failed to post seq %llu\n", S.rank, (unsigned long long)s);
-          S.proxy_err.store(true);
-          return;
-        }
-      continue;
-    }
-    if ((++spin & 1023u) == 0) {
-      const uint64_t done = load_acquire(&S.ctl->done);
-      const auto now = clk::now();
-      if (done != last_done || done >= pub) {
-        last_done = done;
-        last_move = now;
-        reported = false;
-      } else if (!reported && now - last_move > std::chrono::seconds(2)) {
-        reported = true;
-        S.stalls.fetch_add(1);
-        char buf[512];
-        int o = snprintf(buf, sizeof buf, "arx rank %d STALL: published %llu posted %llu done %llu; flags:", S.rank,
-                         (unsigned long long)pub, (unsigned long long)posted, (unsigned long long)done);
-        for (int j = 0; j < S.world && o < (int)sizeof buf; ++j)
-          if (j != S.rank)
-            o += snprintf(buf + o, sizeof buf - o, " r%d=%llu", j, (unsigned long long)load_acquire(&S.flags[j]));
-        fprintf(stderr, "%s\n", buf);
-      }
-    }
-    cpu_relax();
+// Proxy thread (page "arx.cu", proxy_loop): arx::Proxy posts every seq in
+// order up to the target the mode allows and runs the stall watchdog.
+void proxy_main() {
+  if (!S.core->run(S.stop)) {
+    fprintf(stderr, "arx rank %d: proxy failed to post seq %llu\n", S.rank,
+            (unsigned long long)(S.core->posted() + 1));
+    S.proxy_err.store(true);
   }
 }
 
@@ -206,13 +156,11 @@ int init_impl(int world, size_t max_n, int rank) {
   }
   memset((void*)S.ctl, 0, 4096);
   memset((void*)S.flags, 0, 4096);
-  S.posted.store(0);
   S.proxy_err.store(false);
   S.stop.store(false);
-  S.stalls.store(0);
-  S.mode.store(ARX_PROXY_LOCKSTEP);
+  S.core.reset(new arx::Proxy(&S.ctl->seq, &S.ctl->done, S.flags, S.world, S.rank));
   S.timeout_us = 2000000;
-  S.proxy = std::thread(proxy_loop);
+  S.proxy = std::thread(proxy_main);
   S.inited = true;
   return ARX_OK;
 }
@@ -239,6 +187,7 @@ int arx_finalize(void) {
   S.stop.store(true, std::memory_order_release);
   store_release(&S.ctl->stop, 1);
   if (S.proxy.joinable()) S.proxy.join();
+  S.core.reset();
   free_all();
   S.inited = false;
   S.world = S.rank = 0;
@@ -249,8 +198,10 @@ int arx_finalize(void) {
 
 int arx_publish(uint64_t seq) {
   if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
-  std::lock_guard<std::mutex> g(S.publish_mu);
-  return publish_locked(seq);
+  if (!S.core->publish(seq))
+    return fail(ARX_EORDER, "arx_publish(%llu) after %llu: seqs are posted in order", (unsigned long long)seq,
+                (unsigned long long)S.core->posted());
+  return ARX_OK;
 }
 
 int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream) {
@@ -328,7 +279,7 @@ int arx_set_proxy_mode(int mode) {
   if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
   if (mode != ARX_PROXY_LOCKSTEP && mode != ARX_PROXY_RUNAHEAD && mode != ARX_PROXY_MANUAL)
     return fail(ARX_EINVAL, "proxy mode %d unknown", mode);
-  S.mode.store(mode);
+  S.core->mode.store(mode);
   return ARX_OK;
 }
 
@@ -343,7 +294,7 @@ int arx_set_timeout_us(uint64_t us) {
 int arx_status(uint64_t* published, uint64_t* posted, uint64_t* done) {
   if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
   if (published) *published = load_acquire(&S.ctl->seq);
-  if (posted) *posted = S.posted.load();
+  if (posted) *posted = S.core->posted();
   if (done) *done = load_acquire(&S.ctl->done);
   return ARX_OK;
 }
@@ -366,7 +317,7 @@ int arx_debug_state(uint64_t* words, int nwords) {
   all[8] = load_acquire(&S.ctl->done);
   all[9] = load_acquire(&S.ctl->err);
   all[10] = load_acquire(&S.ctl->err_seq);
-  all[11] = S.posted.load();
+  all[11] = S.core->posted();
   for (int i = 0; i < S.world; ++i) all[12 + i] = load_acquire(&S.flags[i]);
   const int total = 12 + S.world;
   const int m = nwords < total ? nwords : total;
