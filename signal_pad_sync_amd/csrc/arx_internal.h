@@ -44,6 +44,7 @@ enum : int {
 
 constexpr int kBlock = 256;       // threads per workgroup of the reduction kernels
 constexpr int kMaxOneShotGrid = 256;  // co-resident workgroups of the one-shot kernel
+constexpr int kOneShotTargetGrid = 64;  // one-shot workgroups the block size aims for
 
 struct OneShotArgs {
   const uint16_t* in;
@@ -77,14 +78,17 @@ struct BarrierArgs {
   Ctl* ctl;
 };
 
-// Launchers (defined in arx_kernels.hip). W in [2, 8].
-hipError_t launch_oneshot(const OneShotArgs& a, int W, hipStream_t stream);
+// Launchers (defined in arx_kernels.hip). W in [2, 8]. block: threads per
+// one-shot workgroup (256, 512 or 1024), or 0 to choose by n.
+hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, hipStream_t stream);
+int oneshot_block(uint32_t n);
 hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t stream);
 hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t stream);
 hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t stream);
 
-// Grid the one-shot kernel uses for n elements (all its workgroups must be
-// resident at once, since they wait on each other).
-unsigned oneshot_grid(uint32_t n);
+// Grid the one-shot kernel uses for n elements with `block` threads per
+// workgroup (all its workgroups must be resident at once, since they wait
+// on each other).
+unsigned oneshot_grid(uint32_t n, int block);
 
 }  // namespace arx

@@ -220,7 +220,7 @@ int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream) {
   a.n = (uint32_t)n;
   a.rank = S.rank;
   a.timeout = timeout_ticks();
-  HIPCHK(arx::launch_oneshot(a, S.world, stream));
+  HIPCHK(arx::launch_oneshot(a, S.world, 0, stream));
   return ARX_OK;
 }
 

@@ -206,6 +206,29 @@ def test_sizes_tails_and_rank(W, rank):
         check_state(st, rank)
 
 
+def test_grid_stride_path():
+    """n beyond one vector per thread of the largest co-resident grid
+    (256 workgroups x 1024 threads x 8 elements = 2 Mi), so each thread
+    loops over several vectors; ragged tail included."""
+    W, rank = 3, 2
+    max_n = (1 << 22) + 64
+    recv = [[WL.normal(7000 + 10 * par + s, max_n) for s in range(W)] for par in (0, 1)]
+    with library(W, max_n, rank=rank):
+        fill_recv(recv, rank)
+        st = None
+        for n in ((1 << 21) + 8, (1 << 22) + 5):
+            x = WL.normal(7100 + n, n)
+            inp, out = to_dev(x, pad_to=max_n), sentinel(max_n)
+            note(f"grid-stride W={W} n={n}")
+            arx.allreduce(inp, out, n)
+            torch.cuda.synchronize()
+            st, outs = P.sequential_model([(x, n)], recv, W, rank=rank, max_n=max_n, state=st)
+            got = to_host(out)
+            assert_bits(got[:n], outs[0], f"grid-stride n={n}")
+            assert np.all(got[n:] == 0xDEAD)
+        check_state(st, rank)
+
+
 def test_in_place():
     """in and out may be the same buffer."""
     W, n = 4, 100003
