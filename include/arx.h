@@ -63,6 +63,8 @@ extern "C" {
 #define ARX_PROXY_LOCKSTEP 0 /* once this rank has published s (peers exactly as fast) */
 #define ARX_PROXY_RUNAHEAD 1 /* once this rank has published s - 1 (the earliest a peer can) */
 #define ARX_PROXY_MANUAL 2   /* never; the caller calls arx_publish */
+#define ARX_PROXY_STRESS 3   /* lockstep, and before posting s the proxy writes the peers' data for s
+                                into recv[s & 1] from the source set by arx_set_stress_source */
 
 /* Barrier memory semantics (page "triton_barrier.py", blockwise_barrier). */
 #define ARX_SEM_RELAXED 0 /* relaxed system-scope CAS on both sides */
@@ -156,6 +158,20 @@ uint32_t* arx_pad_ptr(int rank);
 /* Choose when the proxy posts flags (ARX_PROXY_*). Change it only while no
  * call is in flight. */
 int arx_set_proxy_mode(int mode);
+
+/*
+ * arx_set_stress_source — the data the proxy writes in ARX_PROXY_STRESS
+ * mode, standing for peers whose partials arrive with their flags (page
+ * "arx.cu", protocol comment: the peer writes recv[seq & 1][rank], then the
+ * flag, on one ordered channel). Before posting seq s the proxy copies
+ * pool[s % sets][src] into recv[s & 1][src] for every src != rank on a
+ * stream of its own, waits for the copies, then posts the flags.
+ *   pool: device bf16 [sets][W][max_n], owned by the caller, kept alive and
+ *   unchanged while the mode is in use; sets >= 1. NULL / 0 clears it.
+ * Errors: ARX_ESTATE, ARX_EINVAL, ARX_EHIP. A copy failure during the mode
+ * latches ARX_EPROXY.
+ */
+int arx_set_stress_source(const void* pool, int sets);
 
 /* Bound of every device-side wait, in microseconds (default 2000000, i.e.
  * 2 s; 1 us .. 60 s). Applies to calls launched after it. */

@@ -12,7 +12,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarx.so")
 
 OK, EINVAL, ESTATE, ENOMEM, EHIP, EPROXY, EORDER, ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
-PROXY_LOCKSTEP, PROXY_RUNAHEAD, PROXY_MANUAL = 0, 1, 2
+PROXY_LOCKSTEP, PROXY_RUNAHEAD, PROXY_MANUAL, PROXY_STRESS = 0, 1, 2, 3
 SEM_RELAXED, SEM_ACQ_REL = 0, 1
 MAX_WORLD, MAX_PAD_BLOCKS, MAX_N = 8, 1024, 1 << 30
 
@@ -36,6 +36,7 @@ SIGNATURES = [
     ("arx_send_ptr", _c.c_void_p, [_c.c_int]),
     ("arx_pad_ptr", _c.c_void_p, [_c.c_int]),
     ("arx_set_proxy_mode", _c.c_int, [_c.c_int]),
+    ("arx_set_stress_source", _c.c_int, [_c.c_void_p, _c.c_int]),
     ("arx_set_timeout_us", _c.c_int, [_c.c_uint64]),
     ("arx_status", _c.c_int, [_u64p, _u64p, _u64p]),
     ("arx_debug_state", _c.c_int, [_u64p, _c.c_int]),
@@ -123,6 +124,11 @@ def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, str
 
 def set_proxy_mode(mode: int):
     _check(lib.arx_set_proxy_mode(mode))
+
+
+def set_stress_source(pool, sets: int):
+    """pool: bf16 device tensor [sets, W, max_n] (kept alive by the caller)."""
+    _check(lib.arx_set_stress_source(_ptr(pool), sets))
 
 
 def set_timeout_us(us: int):

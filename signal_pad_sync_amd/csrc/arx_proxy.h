@@ -20,7 +20,7 @@
 
 namespace arx {
 
-enum : int { PROXY_LOCKSTEP = 0, PROXY_RUNAHEAD = 1, PROXY_MANUAL = 2 };
+enum : int { PROXY_LOCKSTEP = 0, PROXY_RUNAHEAD = 1, PROXY_MANUAL = 2, PROXY_STRESS = 3 };
 
 class Proxy {
  public:
@@ -37,6 +37,10 @@ class Proxy {
   std::function<Clock::time_point()> now = [] { return Clock::now(); };
   std::function<void(const std::string&)> report = [](const std::string& s) { fprintf(stderr, "%s\n", s.c_str()); };
   std::chrono::milliseconds stall_after{2000};
+  // Called before seq s is posted in PROXY_STRESS mode, to put the peers'
+  // data for s in place (the data then precedes its flag); false fails the
+  // post.
+  std::function<bool(uint64_t)> before_post;
 
   uint64_t posted() const { return posted_.load(std::memory_order_acquire); }
 
@@ -48,21 +52,24 @@ class Proxy {
     return publish_locked(s);
   }
 
-  // One pass of the loop: post up to the seq the mode allows, or else run
-  // the watchdog check. Returns false if posting failed (an order error,
-  // which cannot happen unless publish() was also called concurrently in a
-  // posting mode).
+  // One pass of the loop: post up to the seq the mode allows (in stress
+  // mode each post is preceded by before_post), or else run the watchdog
+  // check. Returns false if posting failed: before_post failed, or an order
+  // error, which cannot happen unless publish() was also called
+  // concurrently in a posting mode.
   bool step() {
     const uint64_t pub = __atomic_load_n(pub_, __ATOMIC_ACQUIRE);
     const int m = mode.load(std::memory_order_relaxed);
     const uint64_t have = posted();
     uint64_t target = have;
-    if (m == PROXY_LOCKSTEP) target = pub;
+    if (m == PROXY_LOCKSTEP || m == PROXY_STRESS) target = pub;
     else if (m == PROXY_RUNAHEAD) target = pub + 1;
     if (target > have) {
       std::lock_guard<std::mutex> g(mu_);
-      for (uint64_t s = posted() + 1; s <= target; ++s)
+      for (uint64_t s = posted() + 1; s <= target; ++s) {
+        if (m == PROXY_STRESS && before_post && !before_post(s)) return false;
         if (!publish_locked(s)) return false;
+      }
       return true;
     }
     watchdog(pub, have);

@@ -25,7 +25,7 @@ namespace {
 using arx::Ctl;
 
 static_assert(ARX_PROXY_LOCKSTEP == arx::PROXY_LOCKSTEP && ARX_PROXY_RUNAHEAD == arx::PROXY_RUNAHEAD &&
-                  ARX_PROXY_MANUAL == arx::PROXY_MANUAL,
+                  ARX_PROXY_MANUAL == arx::PROXY_MANUAL && ARX_PROXY_STRESS == arx::PROXY_STRESS,
               "proxy mode numbering");
 
 struct State {
@@ -46,6 +46,9 @@ struct State {
   std::thread proxy;
   std::atomic<bool> proxy_err{false};
   std::atomic<bool> stop{false};
+  const uint16_t* stress_pool = nullptr;  // device [sets][W][max_n], caller-owned
+  int stress_sets = 0;
+  hipStream_t stress_stream = nullptr;    // the proxy's own copy stream
 
   // A process that never called arx_finalize still must not end with a
   // joinable thread (that aborts): stop and join the proxy, CPU-side only.
@@ -99,11 +102,29 @@ int check_ready() {
 
 uint64_t timeout_ticks() { return S.timeout_us * S.clock_khz / 1000u; }
 
+// The peers' data for seq s, written before its flag (ARX_PROXY_STRESS).
+bool stress_copy(uint64_t s) {
+  if (!S.stress_pool || !S.stress_stream) return false;
+  const int par = (int)(s & 1);
+  const uint16_t* set = S.stress_pool + (size_t)(s % (uint64_t)S.stress_sets) * S.world * S.max_n;
+  for (int src = 0; src < S.world; ++src) {
+    if (src == S.rank) continue;
+    if (hipMemcpyAsync(S.recv + ((size_t)par * S.world + src) * S.stride, set + (size_t)src * S.max_n,
+                       S.max_n * sizeof(uint16_t), hipMemcpyDeviceToDevice, S.stress_stream) != hipSuccess)
+      return false;
+  }
+  return hipStreamSynchronize(S.stress_stream) == hipSuccess;
+}
+
 void free_all() {
   if (S.send) (void)hipFree(S.send);
   if (S.recv) (void)hipFree(S.recv);
   if (S.pads) (void)hipFree(S.pads);
   if (S.words) (void)hipFree(S.words);
+  if (S.stress_stream) (void)hipStreamDestroy(S.stress_stream);
+  S.stress_stream = nullptr;
+  S.stress_pool = nullptr;
+  S.stress_sets = 0;
   if (S.ctl) (void)hipHostFree(S.ctl);
   if (S.flags) (void)hipHostFree(S.flags);
   S.send = S.recv = nullptr;
@@ -159,6 +180,7 @@ int init_impl(int world, size_t max_n, int rank) {
   S.proxy_err.store(false);
   S.stop.store(false);
   S.core.reset(new arx::Proxy(&S.ctl->seq, &S.ctl->done, S.flags, S.world, S.rank));
+  S.core->before_post = stress_copy;
   S.timeout_us = 2000000;
   S.proxy = std::thread(proxy_main);
   S.inited = true;
@@ -277,9 +299,27 @@ uint32_t* arx_pad_ptr(int rank) {
 
 int arx_set_proxy_mode(int mode) {
   if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
-  if (mode != ARX_PROXY_LOCKSTEP && mode != ARX_PROXY_RUNAHEAD && mode != ARX_PROXY_MANUAL)
+  if (mode != ARX_PROXY_LOCKSTEP && mode != ARX_PROXY_RUNAHEAD && mode != ARX_PROXY_MANUAL &&
+      mode != ARX_PROXY_STRESS)
     return fail(ARX_EINVAL, "proxy mode %d unknown", mode);
+  if (mode == ARX_PROXY_STRESS && !S.stress_pool)
+    return fail(ARX_EINVAL, "stress mode needs arx_set_stress_source first");
   S.core->mode.store(mode);
+  return ARX_OK;
+}
+
+int arx_set_stress_source(const void* pool, int sets) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  if (S.core->mode.load() == ARX_PROXY_STRESS) return fail(ARX_ESTATE, "leave stress mode before changing its source");
+  if (pool == nullptr || sets == 0) {
+    S.stress_pool = nullptr;
+    S.stress_sets = 0;
+    return ARX_OK;
+  }
+  if (sets < 0) return fail(ARX_EINVAL, "sets %d < 0", sets);
+  if (!S.stress_stream) HIPCHK(hipStreamCreateWithFlags(&S.stress_stream, hipStreamNonBlocking));
+  S.stress_pool = (const uint16_t*)pool;
+  S.stress_sets = sets;
   return ARX_OK;
 }
 

@@ -181,6 +181,34 @@ static void scenario_concurrent_publish() {
   printf("ok %s\n", name);
 }
 
+// Stress mode: the data for seq s is written before s is posted, so a
+// device that sees flag s always finds data s.
+static void scenario_stress() {
+  const char* name = "stress";
+  Words w;
+  uint64_t data = 0;
+  arx::Proxy p(&w.pub, &w.done, w.flags, 4, 0);
+  p.before_post = [&](uint64_t s) { __atomic_store_n(&data, s, __ATOMIC_RELEASE); return true; };
+  p.mode = arx::PROXY_STRESS;
+  std::atomic<bool> stop{false};
+  std::thread t([&] { p.run(stop); });
+  bool ok = true;
+  for (uint64_t s = 1; s <= 20000 && ok; ++s) {
+    st(&w.pub, s);
+    while (ld(&w.flags[2]) < s) {}
+    ok = ld(&data) >= s;
+    st(&w.done, s);
+  }
+  stop = true;
+  t.join();
+  CHECK(ok, name, "a flag was seen before its data");
+  arx::Proxy q(&w.pub, &w.done, w.flags, 4, 0);
+  q.before_post = [](uint64_t) { return false; };
+  q.mode = arx::PROXY_STRESS;
+  CHECK(!q.step(), name, "a failed data copy did not fail the post");
+  printf("ok %s\n", name);
+}
+
 int main() {
   scenario_mode("lockstep", arx::PROXY_LOCKSTEP, 0);
   scenario_mode("runahead", arx::PROXY_RUNAHEAD, 1);
@@ -188,5 +216,6 @@ int main() {
   scenario_no_skip_no_lead();
   scenario_watchdog();
   scenario_concurrent_publish();
+  scenario_stress();
   return failures ? 1 : 0;
 }

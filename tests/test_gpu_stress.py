@@ -1,0 +1,65 @@
+"""GPU: peer data written by another agent just before each flag.
+
+Page "arx.cu", protocol comment: a peer writes its partial into
+recv[seq & 1][rank] and then the flag, on one ordered channel, and the GPU
+sums once every flag has reached seq. In stress mode the library's proxy
+plays those peers: before posting seq s it copies a different data set into
+recv[s & 1] on its own stream. The slot of the same parity was last read two
+calls earlier, so a stale cached line would give a wrong sum. Every output is
+compared bit-exact with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import reduce as R
+from signal_pad_sync_amd import arx
+from signal_pad_sync_amd import workloads as WL
+from tests.gpu_util import library, note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("W,n,sets,K", [(8, 131072, 5, 200), (4, 262147, 3, 64), (2, 1000, 7, 100)])
+def test_fresh_peer_data_every_seq(W, n, sets, K):
+    pool = np.stack([np.stack([WL.normal(8000 + 10 * k + src, n) for src in range(W)]) for k in range(sets)])
+    npad = (n + 7) & ~7                               # rows start 16-byte aligned
+    ins = np.zeros((K, npad), np.uint16)
+    for k in range(K):
+        ins[k, :n] = WL.normal(9000 + k + 1, n)
+    with library(W, n):
+        dpool = to_dev(pool.reshape(-1)).view(sets, W, n)
+        arx.set_stress_source(dpool, sets)
+        arx.set_proxy_mode(arx.PROXY_STRESS)
+        din = to_dev(ins.reshape(-1)).view(K, npad)
+        dout = torch.empty_like(din)
+        note(f"stress W={W} n={n} sets={sets}: {K} calls")
+        for k in range(K):
+            arx.allreduce(din[k], dout[k], n)
+        torch.cuda.synchronize()
+        arx.set_proxy_mode(arx.PROXY_LOCKSTEP)
+        got = to_host(dout).reshape(K, npad)[:, :n]
+        d = arx.debug_state()
+        assert d["ctl_err"] == 0 and d["seq_dev"] == K and d["posted"] == K, d
+    for k in range(K):
+        seq = k + 1
+        parts = [ins[k, :n]] + [pool[seq % sets][src] for src in range(1, W)]
+        want = R.reduce(parts, n=n)
+        if not np.array_equal(got[k], want):
+            bad = np.flatnonzero(got[k] != want)
+            raise AssertionError(f"call {seq}: {bad.size} elements differ, first at {bad[0]}")
+
+
+def test_stress_source_rules():
+    with library(2, 64):
+        with pytest.raises(arx.ArxError) as e:
+            arx.set_proxy_mode(arx.PROXY_STRESS)       # no source yet
+        assert e.value.code == arx.EINVAL
+        pool = torch.zeros(2 * 2 * 64, dtype=torch.bfloat16, device="cuda")
+        arx.set_stress_source(pool, 2)
+        arx.set_proxy_mode(arx.PROXY_STRESS)
+        with pytest.raises(arx.ArxError) as e:
+            arx.set_stress_source(pool, 3)             # not while in use
+        assert e.value.code == arx.ESTATE
+        arx.set_proxy_mode(arx.PROXY_LOCKSTEP)
+        arx.set_stress_source(None, 0)
