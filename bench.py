@@ -256,10 +256,11 @@ def main():
         rb = (8 + 1) * 2 * 8192 * 8192
         extra["reduce_128MiB"] = {
             "workload": "W=8, bf16 [8192,8192] per partial, reduction alone",
-            "bytes_per_call": rb, "us_median": round(med, 2), "us_mean_back_to_back": round(mean, 2),
-            "GBps": round(rb / med / 1e3, 1), "frac_of_hbm_peak": round(rb / med / 1e3 / HBM_PEAK_GBS, 4),
+            "bytes_per_call": rb, "us_median_single": round(med, 2), "us_mean_back_to_back": round(mean, 2),
+            "GBps": round(rb / mean / 1e3, 1), "frac_of_hbm_peak": round(rb / mean / 1e3 / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("reduce_kernel_w8_n67108864_bytes")}
-        log(f"  {med:.1f} us median, {rb / med / 1e3:.0f} GB/s")
+        log(f"  {mean:.1f} us per launch back to back ({med:.1f} us median timed one by one), "
+            f"{rb / mean / 1e3:.0f} GB/s")
     if want("barrier"):
         for name, sem in (("acq_rel", arx.SEM_ACQ_REL), ("relaxed", arx.SEM_RELAXED)):
             log(f"blockwise barrier, 256 workgroups, W=8, {name}, 100 launches per hipGraph")
@@ -293,7 +294,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
                      "traffic": recorded_traffic("oneshot_kernel_w8_n131072_bytes"),
-                     "kernel": "oneshot_kernel<8,true>", "bytes_per_launch": bytes_call,
+                     "kernel": "oneshot_kernel<8,true,256>", "bytes_per_launch": bytes_call,
                      "kernel_us": round(us_call, 3) if us_call else None},
         "cpu_baseline": cpu,
         "extra": extra,
