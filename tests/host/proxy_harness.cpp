@@ -65,6 +65,9 @@ static void scenario_mode(const char* name, int mode, uint64_t lead) {
     std::string why;
     const uint64_t K = 20000;
     const bool ok = fake_gpu(w, world, rank, K, lead, why);
+    // run-ahead posts K + 1 after seeing K published: let it finish first
+    const auto t0 = std::chrono::steady_clock::now();
+    while (p.posted() < K + lead && std::chrono::steady_clock::now() - t0 < 5s) {}
     stop = true;
     t.join();
     CHECK(ok, name, "world %d: %s", world, why.c_str());
