@@ -23,6 +23,16 @@ with the HIP library:
     peer's flag never runs more than one seq ahead of this rank's publish.
     Mutants switch off one safety rule each; each must fail.
 
+``check_counter_barrier``
+    Brute-force exploration of the counter barrier (page "common.cuh",
+    Semaphore and PullController::sync): every rank adds 1 to each rank's
+    semaphore flag for its block, then the rank's own lane waits until its
+    flag, minus a base only it keeps, reaches W (start stage) or 2W (end
+    stage); the end stage then advances the base by 2W. Flags only grow.
+    Checks barrier safety per stage (every rank has entered the stage; the
+    stronger per-flag form holds only for W = 2), freedom from deadlock, and
+    the final flag and base values. Mutants C1-C3 must fail.
+
 ``check_barrier``
     Brute-force exploration of the blockwise signal-pad barrier (page
     "triton_barrier.py", send_signal / wait_signal / blockwise_barrier): W
@@ -414,3 +424,113 @@ def barrier_pads_after(W: int, nblocks: int, rounds: int = 1) -> List[np.ndarray
     zero-filled pads: all zero (page "triton_barrier.py", blockwise_barrier
     docstring on graph friendliness)."""
     return [np.zeros((nblocks, W), np.uint32) for _ in range(W)]
+
+
+# --------------------------------------------------------------------------
+# Brute-force interleavings of the counter barrier (two stages per round)
+# --------------------------------------------------------------------------
+
+COUNTER_MUTANTS = {
+    None: "flag - base >= W * stage, end stage advances base by 2W (page common.cuh)",
+    "C1": "the end stage does not advance the base",
+    "C2": "the wait tests flag - base == W * stage instead of >=",
+    "C3": "the start stage also advances the base, by W",
+}
+
+# per-rank program counter within a stage: lanes still to add, then wait
+ADDING, WAITING, STAGE_DONE = range(3)
+
+
+def check_counter_barrier(W: int, K: int, mutant: Optional[str] = None, strong: str = "",
+                          max_states: int = 5_000_000) -> CheckResult:
+    """Explores every interleaving of W ranks running K rounds of (start
+    stage, end stage) on one block id.
+
+    Safety, by default: no rank leaves a stage before every rank has entered
+    it (made at least one of its adds for it). With strong="all" (every
+    stage) or "end" (end stages only, the fenced ones): no rank r leaves such
+    a stage before every rank's add to r's own flag for that stage has
+    happened, which is what a release / acquire pairing through r's flag
+    needs. The weak form holds for any W; the strong form holds for W = 2
+    but not for W >= 3, where a rank that is a stage ahead can add to r's
+    flag in place of a slow rank's pending add.
+
+    State: (stage_idx, added, waiting, flag, base). stage_idx[r] counts the
+    stages rank r has entered (0-based; stage 2k is round k's start, 2k+1
+    its end; 2K once finished); added[r] is the set (bitmask) of lanes of
+    rank r that have added in the current stage; waiting[r] tells whether
+    rank r's own lane is now waiting; flag[r] and base[r] are rank r's
+    semaphore flag and its owner-only base counter.
+    """
+    if mutant not in COUNTER_MUTANTS:
+        raise ValueError(mutant)
+    full = (1 << W) - 1
+    init = ((0,) * W, (0,) * W, (0,) * W, (0,) * W, (0,) * W)
+    seen = {init}
+    stack = [init]
+    finals = 0
+    while stack:
+        st = stack.pop()
+        stage_idx, added, waiting, flag, base = st
+        succ = []
+        for r in range(W):
+            si = stage_idx[r]
+            if si >= 2 * K:
+                continue
+            start = si % 2 == 0
+            # a lane that has not added yet adds 1 to its rank's flag
+            if not waiting[r]:
+                for w in range(W):
+                    if not added[r] >> w & 1:
+                        flag2 = flag[:w] + (flag[w] + 1,) + flag[w + 1:]
+                        added2 = added[:r] + (added[r] | (1 << w),) + added[r + 1:]
+                        waiting2 = waiting
+                        if added2[r] == full:
+                            waiting2 = waiting[:r] + (1,) + waiting[r + 1:]
+                        succ.append((stage_idx, added2, waiting2, flag2, base))
+            else:
+                target = W * (1 if start else 2)
+                have = flag[r] - base[r]
+                ok = have == target if mutant == "C2" else have >= target
+                if ok:
+                    # rank r leaves this stage: every rank must have added for it
+                    for q in range(W):
+                        if strong == "all" or (strong == "end" and not start):
+                            q_added = stage_idx[q] > si or (stage_idx[q] == si and added[q] >> r & 1)
+                        else:
+                            q_added = stage_idx[q] > si or (stage_idx[q] == si and added[q] != 0)
+                        if not q_added:
+                            return CheckResult(False, len(seen), (
+                                f"rank {r} left stage {si} before rank {q} arrived at it"))
+                    b = base[r]
+                    if not start and mutant != "C1":
+                        b = base[r] + 2 * W
+                    if start and mutant == "C3":
+                        b = base[r] + W
+                    base2 = base[:r] + (b,) + base[r + 1:]
+                    stage2 = stage_idx[:r] + (si + 1,) + stage_idx[r + 1:]
+                    added2 = added[:r] + (0,) + added[r + 1:]
+                    waiting2 = waiting[:r] + (0,) + waiting[r + 1:]
+                    succ.append((stage2, added2, waiting2, flag, base2))
+        if not succ:
+            if not all(x == 2 * K for x in stage_idx):
+                return CheckResult(False, len(seen), (
+                    f"deadlock: stages {stage_idx} flags {flag} bases {base}"))
+            if any(f != 2 * W * K for f in flag) or any(b != 2 * W * K for b in base):
+                return CheckResult(False, len(seen), f"final flags {flag} bases {base}, want {2 * W * K}")
+            finals += 1
+        for s2 in succ:
+            if s2 not in seen:
+                seen.add(s2)
+                stack.append(s2)
+                if len(seen) > max_states:
+                    raise RuntimeError(f"state space exceeds {max_states}")
+    return CheckResult(True, len(seen), None, finals)
+
+
+def epochs_after(launches: int) -> int:
+    """Page "common.cuh", PushController: each launch's exit flips a block's
+    epoch between 0 and 1 (kNumStages = 2), so after k launches from 0 the
+    epoch is k mod 2 and launch i (0-based) saw epoch i mod 2."""
+    return launches % 2
+

@@ -99,3 +99,35 @@ def test_sequential_model_manual_needs_flags():
     recv = _recv(1, W, n)
     with pytest.raises(RuntimeError):
         P.sequential_model([(recv[1][0], n)], recv, W, mode=P.MANUAL)
+
+
+@pytest.mark.parametrize("W,K", [(2, 1), (2, 3), (3, 1), (3, 2), (3, 3)])
+def test_counter_barrier_safe_live_and_final(W, K):
+    """Page "common.cuh", PullController::sync: every rank has entered a
+    stage before any rank leaves it; no deadlock; flags end at 2WK and each
+    owner's base follows them."""
+    r = P.check_counter_barrier(W, K)
+    assert r.ok, r.violation
+    assert r.finals == 1
+
+
+@pytest.mark.parametrize("mutant", ["C1", "C2", "C3"])
+def test_counter_barrier_mutants_are_caught(mutant):
+    assert not P.check_counter_barrier(2, 2, mutant=mutant).ok
+    assert not P.check_counter_barrier(3, 2, mutant=mutant).ok
+
+
+def test_counter_barrier_per_flag_pairing():
+    """The stronger property a fenced end stage needs (every rank's add to
+    my own flag for this stage happened before I leave) holds at W = 2 for
+    any number of rounds, and for one round at any W, but not at W = 3 over
+    two rounds: a rank already in the next round's start stage adds to my
+    flag in place of a slow rank's pending end-stage add."""
+    assert P.check_counter_barrier(2, 3, strong="all").ok
+    assert P.check_counter_barrier(3, 1, strong="end").ok
+    r = P.check_counter_barrier(3, 2, strong="end")
+    assert not r.ok and "left stage 1" in r.violation
+
+
+def test_epochs_alternate():
+    assert [P.epochs_after(k) for k in range(5)] == [0, 1, 0, 1, 0]
