@@ -154,8 +154,9 @@ def bench_reduce(args):
 
 
 def bench_barrier(args, sem):
-    """256-workgroup blockwise barrier at W=8, 100 launches per hipGraph;
-    returns microseconds per launch."""
+    """256-workgroup barrier at W=8, 100 launches per hipGraph; returns
+    microseconds per launch. sem: a signal-pad semantics, or "counter" for
+    one round (start + end stage) of the counter barrier."""
     import torch
     from signal_pad_sync_amd import arx
     arx.init(8, 1024)
@@ -165,7 +166,10 @@ def bench_barrier(args, sem):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(per):
-                arx.barrier_blockwise(256, sem, 1)
+                if sem == "counter":
+                    arx.counter_barrier(256, 1)
+                else:
+                    arx.barrier_blockwise(256, sem, 1)
         for _ in range(3):
             g.replay()
         reps = max(1, args.steps // per)
@@ -262,8 +266,8 @@ def main():
         log(f"  {mean:.1f} us per launch back to back ({med:.1f} us median timed one by one), "
             f"{rb / mean / 1e3:.0f} GB/s")
     if want("barrier"):
-        for name, sem in (("acq_rel", arx.SEM_ACQ_REL), ("relaxed", arx.SEM_RELAXED)):
-            log(f"blockwise barrier, 256 workgroups, W=8, {name}, 100 launches per hipGraph")
+        for name, sem in (("acq_rel", arx.SEM_ACQ_REL), ("relaxed", arx.SEM_RELAXED), ("counter", "counter")):
+            log(f"barrier ({name}), 256 workgroups, W=8, 100 launches per hipGraph")
             us_b = bench_barrier(args, sem)
             extra[f"barrier_256wg_{name}_us"] = round(us_b, 3)
             log(f"  {us_b:.3f} us/launch")

@@ -143,6 +143,32 @@ int arx_reduce(const void* in, void* out, size_t n, int par, hipStream_t stream)
  */
 int arx_barrier_blockwise(int nblocks, int sem, int rounds, hipStream_t stream);
 
+/*
+ * arx_counter_barrier — the counter barrier and per-block epochs of page
+ * "common.cuh" (Semaphore, PullController::sync, PushController) for the W
+ * virtual ranks: launch `nblocks` workgroups of one wave; in workgroup b,
+ * lanes [v*W, v*W + W) play rank v. Each workgroup records its epoch in
+ * seen[b] (if seen is not NULL), runs `rounds` rounds of a start stage
+ * (every rank adds 1 to block b's flag of every rank, the owner waits for
+ * flag - base >= W) and a fenced end stage (waits for flag - base >= 2W,
+ * then advances its base by 2W), then flips its epoch between 0 and 1.
+ * Flags only grow: after R rounds in total, every flag and base of the
+ * blocks used is 2 * W * R.
+ *   nblocks: 1..ARX_MAX_PAD_BLOCKS.  rounds: 0..64.  seen: device u32
+ *   [nblocks] or NULL.
+ * Errors: ARX_ESTATE, ARX_EINVAL, ARX_ETIMEOUT (latched), ARX_EHIP.
+ */
+int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t stream);
+
+/* Device address of rank `rank`'s semaphores: ARX_MAX_PAD_BLOCKS entries of
+ * 32 u32 (128 bytes), flag at [0] and base at [1]; NULL if not initialised
+ * or rank out of range. */
+const uint32_t* arx_sem_ptr(int rank);
+
+/* Device address of the per-block epochs, u32 [ARX_MAX_PAD_BLOCKS]; NULL if
+ * not initialised. */
+const uint32_t* arx_epoch_ptr(void);
+
 /* Device address of recv slot [par][src] (max_n bf16), where the caller puts
  * peer src's partial for parity par; NULL if not initialised or out of range
  * (par not in {0,1}, src not in [0, W)). The slot at src == rank is unused. */

@@ -32,6 +32,9 @@ SIGNATURES = [
     ("arx_allreduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     ("arx_reduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_void_p]),
     ("arx_barrier_blockwise", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
+    ("arx_counter_barrier", _c.c_int, [_c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p]),
+    ("arx_sem_ptr", _c.c_void_p, [_c.c_int]),
+    ("arx_epoch_ptr", _c.c_void_p, []),
     ("arx_recv_ptr", _c.c_void_p, [_c.c_int, _c.c_int]),
     ("arx_send_ptr", _c.c_void_p, [_c.c_int]),
     ("arx_pad_ptr", _c.c_void_p, [_c.c_int]),
@@ -120,6 +123,22 @@ def reduce(inp, out, par: int, n: int = None, stream=None):
 
 def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, stream=None):
     _check(lib.arx_barrier_blockwise(nblocks, sem, rounds, _stream(stream)))
+
+
+def counter_barrier(nblocks: int, rounds: int = 1, seen=None, stream=None):
+    """seen: optional int32 device tensor [nblocks] receiving each block's epoch."""
+    _check(lib.arx_counter_barrier(nblocks, rounds, _ptr(seen), _stream(stream)))
+
+
+def sem_view(rank: int):
+    """int32 tensor viewing rank `rank`'s semaphores, shape [MAX_PAD_BLOCKS, 32]
+    (flag in column 0, base in column 1)."""
+    return _view(lib.arx_sem_ptr(rank), MAX_PAD_BLOCKS * 32, "<i4", None).view(MAX_PAD_BLOCKS, 32)
+
+
+def epoch_view():
+    """int32 tensor viewing the per-block epochs, shape [MAX_PAD_BLOCKS]."""
+    return _view(lib.arx_epoch_ptr(), MAX_PAD_BLOCKS, "<i4", None)
 
 
 def set_proxy_mode(mode: int):

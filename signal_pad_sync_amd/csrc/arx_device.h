@@ -203,4 +203,64 @@ __device__ __forceinline__ bool barrier_blockwise(const Pads& p, uint32_t block_
                              timeout);
 }
 
+// ---- counter barrier and per-block epochs --------------------------------
+
+// Page "common.cuh", struct Semaphore: a flag every rank adds to and a base
+// count only the owning rank reads and writes, on a 128-byte line of its own.
+struct alignas(128) Semaphore {
+  uint32_t flag;
+  uint32_t base;
+  uint32_t pad[30];
+};
+static_assert(sizeof(Semaphore) == 128, "Semaphore layout");
+
+__device__ __forceinline__ Semaphore* select_sem(Semaphore* const (&sem)[8], int i) {
+  Semaphore* r = sem[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) r = (i == k) ? sem[k] : r;
+  return r;
+}
+
+// Page "common.cuh", PullController::sync, one stage: lane `lane` < world
+// adds 1 to block `block_id`'s flag of rank `lane`; the lane whose index is
+// the caller's rank then waits until its own flag minus its base reaches
+// world (start stage) or 2 * world (end stage), and an end stage advances
+// the base by 2 * world. Flags only grow, so no reset is needed between
+// rounds. `fence` makes the add a release and the wait an acquire (system
+// scope); the page allows it on end stages only. The caller places the
+// workgroup barriers: before a fenced or end stage, after a start stage.
+// Returns false if the wait gave up after `timeout` wall-clock ticks.
+__device__ __forceinline__ bool counter_sync(Semaphore* const (&sem)[8], int world, uint32_t block_id, int rank,
+                                             int lane, bool fence, bool start, uint64_t timeout) {
+  if (lane >= world) return true;
+  uint32_t* flag = &(select_sem(sem, lane) + block_id)->flag;
+  if (fence) __hip_atomic_fetch_add(flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  else __hip_atomic_fetch_add(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (lane != rank) return true;
+  Semaphore* own = select_sem(sem, rank) + block_id;
+  const uint32_t target = (uint32_t)world * (start ? 1u : 2u);
+  const uint32_t base = own->base;          // owner-only: a plain load
+  const uint64_t t0 = now_ticks();
+  while (load_relaxed_system(&own->flag) - base < target) {
+    if (now_ticks() - t0 > timeout) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (fence) fence_acquire_system();
+  if (!start) own->base = base + target;    // owner-only: a plain store
+  return true;
+}
+
+// Page "common.cuh", PushController: a per-block epoch that alternates
+// between 0 and 1 at every kernel exit, so consecutive launches can pick
+// alternate buffers per block with no host involvement.
+__device__ __forceinline__ uint32_t block_epoch(const uint32_t* epochs, uint32_t block_id) {
+  return epochs[block_id];
+}
+// Call after the block's last access of its epoch-selected buffers: a
+// workgroup barrier, then thread 0 flips the epoch.
+__device__ __forceinline__ void block_epoch_exit(uint32_t* epochs, uint32_t block_id) {
+  __syncthreads();
+  if (threadIdx.x == 0) epochs[block_id] = (epochs[block_id] + 1u) % 2u;
+}
+
 }  // namespace arx

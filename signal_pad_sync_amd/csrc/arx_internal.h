@@ -8,6 +8,8 @@
 
 namespace arx {
 
+struct Semaphore;
+
 // Control block in pinned, coherent host memory (page "arx.cu": struct Ctl).
 // Line 0 is written by the GPU when it publishes and read by the proxy;
 // line 1 is written by the GPU when a call finishes or a wait times out;
@@ -30,6 +32,7 @@ enum : uint64_t {
   ERR_FLAG_TIMEOUT = 1,     // workgroup 0 gave up waiting for a peer flag
   ERR_GO_TIMEOUT = 2,       // a workgroup gave up waiting for go
   ERR_BARRIER_TIMEOUT = 3,  // a signal-pad CAS wait gave up
+  ERR_COUNTER_TIMEOUT = 4,  // a counter-barrier wait gave up
 };
 
 // Device words (u32), each on its own 256-byte line of one allocation.
@@ -78,12 +81,23 @@ struct BarrierArgs {
   Ctl* ctl;
 };
 
+struct CounterArgs {
+  Semaphore* sem[8];   // rank r's semaphores, one per block id
+  uint32_t* epochs;    // one per block id
+  uint32_t* seen;      // seen[b] = the epoch block b read (for checks), or null
+  int world;
+  int rounds;
+  uint64_t timeout;
+  Ctl* ctl;
+};
+
 // Launchers (defined in arx_kernels.hip). W in [2, 8]. block: threads per
 // one-shot workgroup (256, 512 or 1024), or 0 to choose by n.
 hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, hipStream_t stream);
 int oneshot_block(uint32_t n);
 hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t stream);
 hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t stream);
+hipError_t launch_counter_barrier(const CounterArgs& a, int nblocks, hipStream_t stream);
 hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t stream);
 
 // Grid the one-shot kernel uses for n elements with `block` threads per

@@ -345,6 +345,41 @@ hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- counter barrier and per-block epochs for W virtual ranks -------------
+
+// Workgroup b is one wave; lanes [v * W, v * W + W) play virtual rank v. The
+// block reads its epoch first, runs `rounds` rounds of a start stage
+// (unfenced) and an end stage (fenced) on block id b as the page's
+// PullController does, then flips its epoch as PushController::exit does.
+__global__ __launch_bounds__(64) void counter_barrier_kernel(CounterArgs a) {
+  const int W = a.world;
+  const int t = threadIdx.x;
+  const int v = t / W, s = t - v * W;
+  const bool active = t < W * W;
+  if (threadIdx.x == 0 && a.seen) a.seen[blockIdx.x] = block_epoch(a.epochs, blockIdx.x);
+  for (int r = 0; r < a.rounds; ++r) {
+    // start stage: no fence, workgroup barrier after
+    bool ok = !active || counter_sync(a.sem, W, blockIdx.x, v, s, false, true, a.timeout);
+    if (__syncthreads_or(!ok)) {
+      if (threadIdx.x == 0) report_error(a.ctl, ERR_COUNTER_TIMEOUT, (uint64_t)blockIdx.x);
+      return;
+    }
+    // end stage: workgroup barrier before, fenced
+    __syncthreads();
+    ok = !active || counter_sync(a.sem, W, blockIdx.x, v, s, true, false, a.timeout);
+    if (__syncthreads_or(!ok)) {
+      if (threadIdx.x == 0) report_error(a.ctl, ERR_COUNTER_TIMEOUT, (uint64_t)blockIdx.x);
+      return;
+    }
+  }
+  block_epoch_exit(a.epochs, blockIdx.x);
+}
+
+hipError_t launch_counter_barrier(const CounterArgs& a, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL(counter_barrier_kernel, dim3(nblocks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
 // ---- the rounding alone ------------------------------------------------------
 
 __global__ __launch_bounds__(kBlock) void round_test_kernel(const uint32_t* in, uint16_t* out, size_t n) {

@@ -17,6 +17,7 @@
 #include <thread>
 
 #include "arx.h"
+#include "arx_device.h"
 #include "arx_internal.h"
 #include "arx_proxy.h"
 
@@ -35,6 +36,8 @@ struct State {
   uint16_t* send = nullptr;   // device [2][stride]
   uint16_t* recv = nullptr;   // device [2][W][stride]
   uint32_t* pads = nullptr;   // device [W][ARX_MAX_PAD_BLOCKS][W]
+  arx::Semaphore* sems = nullptr;  // device [W][ARX_MAX_PAD_BLOCKS]
+  uint32_t* epochs = nullptr;      // device [ARX_MAX_PAD_BLOCKS]
   uint32_t* words = nullptr;  // device [WORDS_TOTAL]
   Ctl* ctl = nullptr;         // pinned, host address
   uint64_t* flags = nullptr;  // pinned, host address [8]
@@ -120,6 +123,10 @@ void free_all() {
   if (S.send) (void)hipFree(S.send);
   if (S.recv) (void)hipFree(S.recv);
   if (S.pads) (void)hipFree(S.pads);
+  if (S.sems) (void)hipFree(S.sems);
+  if (S.epochs) (void)hipFree(S.epochs);
+  S.sems = nullptr;
+  S.epochs = nullptr;
   if (S.words) (void)hipFree(S.words);
   if (S.stress_stream) (void)hipStreamDestroy(S.stress_stream);
   S.stress_stream = nullptr;
@@ -152,12 +159,15 @@ int init_impl(int world, size_t max_n, int rank) {
   const size_t recv_b = 2 * (size_t)world * S.stride * sizeof(uint16_t);
   const size_t pads_b = (size_t)world * ARX_MAX_PAD_BLOCKS * world * sizeof(uint32_t);
   const size_t words_b = arx::WORDS_TOTAL * sizeof(uint32_t);
+  const size_t sems_b = (size_t)world * ARX_MAX_PAD_BLOCKS * sizeof(arx::Semaphore);
+  const size_t epochs_b = ARX_MAX_PAD_BLOCKS * sizeof(uint32_t);
   int rc = ARX_OK;
   hipError_t e;
   if ((e = hipMalloc(&S.send, send_b)) != hipSuccess || (e = hipMalloc(&S.recv, recv_b)) != hipSuccess ||
-      (e = hipMalloc(&S.pads, pads_b)) != hipSuccess || (e = hipMalloc(&S.words, words_b)) != hipSuccess) {
-    rc = fail(ARX_ENOMEM, "device allocation of %zu bytes failed: %s", send_b + recv_b + pads_b + words_b,
-              hipGetErrorString(e));
+      (e = hipMalloc(&S.pads, pads_b)) != hipSuccess || (e = hipMalloc(&S.words, words_b)) != hipSuccess ||
+      (e = hipMalloc(&S.sems, sems_b)) != hipSuccess || (e = hipMalloc(&S.epochs, epochs_b)) != hipSuccess) {
+    rc = fail(ARX_ENOMEM, "device allocation of %zu bytes failed: %s",
+              send_b + recv_b + pads_b + words_b + sems_b + epochs_b, hipGetErrorString(e));
   } else if ((e = hipHostMalloc((void**)&S.ctl, 4096, hipHostMallocCoherent | hipHostMallocMapped)) !=
                  hipSuccess ||
              (e = hipHostMalloc((void**)&S.flags, 4096, hipHostMallocCoherent | hipHostMallocMapped)) !=
@@ -165,7 +175,8 @@ int init_impl(int world, size_t max_n, int rank) {
     rc = fail(ARX_ENOMEM, "pinned allocation failed: %s", hipGetErrorString(e));
   } else if ((e = hipMemset(S.send, 0, send_b)) != hipSuccess || (e = hipMemset(S.recv, 0, recv_b)) != hipSuccess ||
              (e = hipMemset(S.pads, 0, pads_b)) != hipSuccess ||
-             (e = hipMemset(S.words, 0, words_b)) != hipSuccess ||
+             (e = hipMemset(S.words, 0, words_b)) != hipSuccess || (e = hipMemset(S.sems, 0, sems_b)) != hipSuccess ||
+             (e = hipMemset(S.epochs, 0, epochs_b)) != hipSuccess ||
              (e = hipHostGetDevicePointer((void**)&S.ctl_dev, S.ctl, 0)) != hipSuccess ||
              (e = hipHostGetDevicePointer((void**)&S.flags_dev, S.flags, 0)) != hipSuccess ||
              (e = hipDeviceSynchronize()) != hipSuccess) {
@@ -281,6 +292,31 @@ int arx_barrier_blockwise(int nblocks, int sem, int rounds, hipStream_t stream) 
   HIPCHK(arx::launch_barrier(a, nblocks, stream));
   return ARX_OK;
 }
+
+int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t stream) {
+  int rc = check_ready();
+  if (rc != ARX_OK) return rc;
+  if (nblocks < 1 || nblocks > ARX_MAX_PAD_BLOCKS)
+    return fail(ARX_EINVAL, "nblocks %d not in [1, %d]", nblocks, ARX_MAX_PAD_BLOCKS);
+  if (rounds < 0 || rounds > 64) return fail(ARX_EINVAL, "rounds %d not in [0, 64]", rounds);
+  arx::CounterArgs a;
+  for (int i = 0; i < 8; ++i) a.sem[i] = i < S.world ? S.sems + (size_t)i * ARX_MAX_PAD_BLOCKS : nullptr;
+  a.epochs = S.epochs;
+  a.seen = seen;
+  a.world = S.world;
+  a.rounds = rounds;
+  a.timeout = timeout_ticks();
+  a.ctl = S.ctl_dev;
+  HIPCHK(arx::launch_counter_barrier(a, nblocks, stream));
+  return ARX_OK;
+}
+
+const uint32_t* arx_sem_ptr(int rank) {
+  if (!S.inited || rank < 0 || rank >= S.world) return nullptr;
+  return reinterpret_cast<const uint32_t*>(S.sems + (size_t)rank * ARX_MAX_PAD_BLOCKS);
+}
+
+const uint32_t* arx_epoch_ptr(void) { return S.inited ? S.epochs : nullptr; }
 
 void* arx_recv_ptr(int par, int src) {
   if (!S.inited || (par != 0 && par != 1) || src < 0 || src >= S.world) return nullptr;

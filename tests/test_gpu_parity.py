@@ -313,3 +313,29 @@ def test_barrier_leaves_pads_zero(W):
                 for r in range(W):
                     assert int(arx.pad_view(r).abs().sum()) == 0
                 assert arx.debug_state()["ctl_err"] == 0
+
+
+@pytest.mark.parametrize("W", [2, 3, 4, 8])
+def test_counter_barrier_flags_bases_epochs(W):
+    """Page "common.cuh": after R rounds (start + end stage) on a block, every
+    rank's flag and base for that block are 2WR (flags only grow, the base
+    follows in the end stage); each launch flips the block's epoch, and each
+    block saw the epoch of its previous launches' parity."""
+    with library(W, 1024):
+        rounds_done = np.zeros(1024, np.int64)
+        launches = np.zeros(1024, np.int64)
+        seen = torch.full((1024,), -1, dtype=torch.int32, device="cuda")
+        for nblocks, rounds in [(1, 1), (256, 1), (256, 3), (1024, 2), (256, 0), (1024, 64), (7, 5)]:
+            note(f"counter barrier W={W} nblocks={nblocks} rounds={rounds}")
+            arx.counter_barrier(nblocks, rounds, seen[:nblocks])
+            torch.cuda.synchronize()
+            got_seen = seen[:nblocks].cpu().numpy()
+            assert np.array_equal(got_seen, launches[:nblocks] % 2), (nblocks, rounds)
+            rounds_done[:nblocks] += rounds
+            launches[:nblocks] += 1
+            for r in range(W):
+                sem = arx.sem_view(r).cpu().numpy()
+                assert np.array_equal(sem[:, 0], 2 * W * rounds_done), f"flags of rank {r}"
+                assert np.array_equal(sem[:, 1], 2 * W * rounds_done), f"bases of rank {r}"
+            assert np.array_equal(arx.epoch_view().cpu().numpy(), launches % 2)
+            assert arx.debug_state()["ctl_err"] == 0
