@@ -33,6 +33,14 @@ with the HIP library:
     stronger per-flag form holds only for W = 2), freedom from deadlock, and
     the final flag and base values. Mutants C1-C3 must fail.
 
+``check_symm_patterns``
+    Brute-force exploration of a symmetric-buffer exchange fenced by the
+    pad barrier's usage patterns (page "triton_barrier.py", blockwise_barrier
+    docstring): each iteration a rank writes its own buffer, passes a
+    barrier (pattern 1, publishing the write), reads every rank's buffer,
+    and passes a barrier (pattern 2, so the next iteration's write cannot
+    clobber a buffer a peer still reads). Mutants P1 / P2 drop one barrier.
+
 ``check_barrier``
     Brute-force exploration of the blockwise signal-pad barrier (page
     "triton_barrier.py", send_signal / wait_signal / blockwise_barrier): W
@@ -533,4 +541,97 @@ def epochs_after(launches: int) -> int:
     epoch between 0 and 1 (kNumStages = 2), so after k launches from 0 the
     epoch is k mod 2 and launch i (0-based) saw epoch i mod 2."""
     return launches % 2
+
+
+# --------------------------------------------------------------------------
+# Brute-force interleavings of a pattern-fenced symmetric-buffer exchange
+# --------------------------------------------------------------------------
+
+SYMM_MUTANTS = {
+    None: "write, barrier (pattern 1), read all, barrier (pattern 2)",
+    "P1": "no barrier between the write and the reads",
+    "P2": "no barrier between the reads and the next iteration's write",
+}
+
+# rank program counter within an iteration
+S_WRITE, S_B1_SEND, S_B1_WAIT, S_READ, S_B2_SEND, S_B2_WAIT, S_NEXT = range(7)
+
+
+def check_symm_patterns(W: int, iters: int, mutant: Optional[str] = None,
+                        max_states: int = 5_000_000) -> CheckResult:
+    """Explores every interleaving of W ranks (one block each, its W barrier
+    lanes modelled as one send step per peer and one consume step per peer)
+    running `iters` iterations of the exchange. A read of rank j's buffer in
+    iteration k must see exactly the tag (j, k).
+
+    State: (pc, it, sent, consumed, pad, buf) per rank: pc and iteration,
+    bitmasks of the peers signalled / consumed in the current barrier, the
+    pad slots (pad[r*W+s] = rank r's slot for rank s), and buf[r] = the tag
+    rank r last wrote.
+    """
+    if mutant not in SYMM_MUTANTS:
+        raise ValueError(mutant)
+    full = (1 << W) - 1
+    init = ((S_WRITE,) * W, (0,) * W, (0,) * W, (0,) * W, (0,) * (W * W), (-1,) * W)
+    seen = {init}
+    stack = [init]
+    finals = 0
+
+    def setr(t, r, v):
+        return t[:r] + (v,) + t[r + 1:]
+
+    while stack:
+        st = stack.pop()
+        pc, it, sent, cons, pad, buf = st
+        succ = []
+        for r in range(W):
+            p, k = pc[r], it[r]
+            if k >= iters:
+                continue
+            if p == S_WRITE:
+                nxt = S_READ if mutant == "P1" else S_B1_SEND
+                succ.append((setr(pc, r, nxt), it, sent, cons, pad, setr(buf, r, r * 64 + k)))
+            elif p in (S_B1_SEND, S_B2_SEND):
+                for s_ in range(W):                 # lane s_ signals rank s_
+                    if not sent[r] >> s_ & 1:
+                        i = s_ * W + r
+                        if pad[i] == 0:             # CAS 0 -> 1
+                            sent2 = setr(sent, r, sent[r] | (1 << s_))
+                            pc2 = setr(pc, r, p + 1) if sent2[r] == full else pc
+                            succ.append((pc2, it, sent2 if sent2[r] != full else setr(sent, r, 0),
+                                         cons, setr(pad, i, 1), buf))
+            elif p in (S_B1_WAIT, S_B2_WAIT):
+                for s_ in range(W):                 # lane s_ consumes rank s_'s signal
+                    if not cons[r] >> s_ & 1:
+                        i = r * W + s_
+                        if pad[i] == 1:             # CAS 1 -> 0
+                            cons2 = setr(cons, r, cons[r] | (1 << s_))
+                            if cons2[r] == full:
+                                nxt = S_READ if p == S_B1_WAIT else S_NEXT
+                                succ.append((setr(pc, r, nxt), it, sent, setr(cons, r, 0), setr(pad, i, 0), buf))
+                            else:
+                                succ.append((pc, it, sent, cons2, setr(pad, i, 0), buf))
+            elif p == S_READ:
+                for j in range(W):
+                    if buf[j] != j * 64 + k:
+                        return CheckResult(False, len(seen), (
+                            f"rank {r} iteration {k} read rank {j}'s buffer holding "
+                            f"{'nothing' if buf[j] < 0 else f'iteration {buf[j] % 64}'}"))
+                nxt = S_NEXT if mutant == "P2" else S_B2_SEND
+                succ.append((setr(pc, r, nxt), it, sent, cons, pad, buf))
+            elif p == S_NEXT:
+                succ.append((setr(pc, r, S_WRITE), setr(it, r, k + 1), sent, cons, pad, buf))
+        if not succ:
+            if not all(x >= iters for x in it):
+                return CheckResult(False, len(seen), f"deadlock: pcs {pc} iterations {it} pad {pad}")
+            if any(pad):
+                return CheckResult(False, len(seen), f"pad not zero at the end: {pad}")
+            finals += 1
+        for s2 in succ:
+            if s2 not in seen:
+                seen.add(s2)
+                stack.append(s2)
+                if len(seen) > max_states:
+                    raise RuntimeError(f"state space exceeds {max_states}")
+    return CheckResult(True, len(seen), None, finals)
 

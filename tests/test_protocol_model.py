@@ -131,3 +131,23 @@ def test_counter_barrier_per_flag_pairing():
 
 def test_epochs_alternate():
     assert [P.epochs_after(k) for k in range(5)] == [0, 1, 0, 1, 0]
+
+
+@pytest.mark.parametrize("W,iters", [(2, 1), (2, 3), (3, 1), (3, 2)])
+def test_symm_patterns_safe(W, iters):
+    """Page "triton_barrier.py", usage patterns: write, acq_rel barrier, read
+    every rank's buffer, relaxed barrier; every read sees its iteration's
+    data, nothing deadlocks, pads end zero."""
+    r = P.check_symm_patterns(W, iters)
+    assert r.ok, r.violation
+    assert r.finals == 1
+
+
+def test_symm_pattern_mutants():
+    """Without pattern 1 a rank reads a buffer before its owner wrote it;
+    without pattern 2 a fast rank overwrites its buffer with the next
+    iteration while a peer still reads the current one."""
+    p1 = P.check_symm_patterns(2, 2, mutant="P1")
+    assert not p1.ok and "holding nothing" in p1.violation
+    p2 = P.check_symm_patterns(2, 2, mutant="P2")
+    assert not p2.ok and "holding iteration 1" in p2.violation
