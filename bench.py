@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--reduce-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,graph,reduce,barrier")
+    ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,graph,reduce,barrier,symm")
     return ap.parse_args()
 
 
@@ -198,6 +198,28 @@ def bench_copy(args):
     return 2 * n * 2, us
 
 
+def bench_symm(args):
+    """Symmetric-buffer all-reduce among the 8 virtual ranks, n=131072, 100
+    iterations in one launch; returns microseconds per iteration."""
+    import torch
+    from signal_pad_sync_amd import arx
+    W, n, iters = 8, 131072, 100
+    arx.init(W, n)
+    try:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(5000)
+        inp = torch.randn(iters * W * n, generator=g, device="cuda").to(torch.bfloat16).view(iters, W, n)
+        out = torch.empty_like(inp)
+        stream = torch.cuda.current_stream()
+        arx.symm_allreduce(inp, out, n, iters)
+        us = timed(lambda: arx.symm_allreduce(inp, out, n, iters), 5, stream) / 5
+        assert arx.debug_state()["ctl_err"] == 0
+    finally:
+        torch.cuda.synchronize()
+        arx.finalize()
+    return us / iters
+
+
 def cpu_baseline(seconds):
     """The oracle's one-shot model (sequential protocol + C reduction) on the
     headline workload, single-threaded, for about `seconds` of CPU time."""
@@ -271,6 +293,12 @@ def main():
             us_b = bench_barrier(args, sem)
             extra[f"barrier_256wg_{name}_us"] = round(us_b, 3)
             log(f"  {us_b:.3f} us/launch")
+
+    if want("symm"):
+        log("symmetric-buffer all-reduce among 8 virtual ranks, n=131072, 100 iterations per launch")
+        us_s = bench_symm(args)
+        extra["symm_w8_n131072_us_per_iteration"] = round(us_s, 3)
+        log(f"  {us_s:.2f} us per iteration")
 
     cpu = None
     if not args.skip_cpu:

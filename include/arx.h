@@ -77,8 +77,10 @@ extern "C" {
  * thread started). This GPU is rank 0.
  *   world: W in [2, 8].  max_n: largest n any later call may use, in bf16
  *   elements, 1 <= max_n <= ARX_MAX_N.
- * Allocates on the current HIP device: send slots [2][max_n] and recv slots
- * [2][W][max_n] bf16 in device memory, W signal pads u32[ARX_MAX_PAD_BLOCKS][W],
+ * Allocates on the current HIP device: send slots [2][max_n], recv slots
+ * [2][W][max_n] and symmetric buffers [W][max_n] bf16 in device memory, W
+ * signal pads u32[ARX_MAX_PAD_BLOCKS][W], W x ARX_MAX_PAD_BLOCKS semaphores
+ * and ARX_MAX_PAD_BLOCKS epochs,
  * the device words (seq, two counters, go, abort), and in pinned coherent
  * host memory the control block and flags[W] (u64). Errors: ARX_EINVAL,
  * ARX_ESTATE (already initialised), ARX_ENOMEM, ARX_EHIP.
@@ -159,6 +161,27 @@ int arx_barrier_blockwise(int nblocks, int sem, int rounds, hipStream_t stream);
  * Errors: ARX_ESTATE, ARX_EINVAL, ARX_ETIMEOUT (latched), ARX_EHIP.
  */
 int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t stream);
+
+/*
+ * arx_symm_allreduce — an all-reduce among the W virtual ranks of this GPU
+ * through symmetric buffers, fenced by the blockwise barrier's usage
+ * patterns (page "triton_barrier.py", blockwise_barrier docstring): one
+ * kernel of W * G workgroups (G per rank, all resident); at its start
+ * pattern 0; then for each of `iters` iterations every rank writes its
+ * partial into its own symmetric buffer, passes pattern 1 (acq_rel, which
+ * publishes the write to the matching blocks), reads its slice of every
+ * rank's buffer, writes the rank-ordered sum (the same reduction as
+ * arx_allreduce), and passes pattern 2 (relaxed, so the next iteration's
+ * write cannot overwrite a slice a peer still reads).
+ *   inputs:  device bf16 [iters][W][ld]; rank v's partial for iteration k
+ *            starts at element (k * W + v) * ld.
+ *   outputs: device bf16 [iters][W][ld], same layout; every rank's result.
+ *   n <= max_n; ld >= n and a multiple of 8; both pointers 16-byte aligned;
+ *   iters in [1, 65536]. Uses the signal pads (block ids 0..G-1) and the
+ *   library's symmetric buffers [W][max_n], allocated by arx_init.
+ * Errors: ARX_ESTATE, ARX_EINVAL, ARX_ETIMEOUT (latched), ARX_EHIP.
+ */
+int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, int iters, hipStream_t stream);
 
 /* Device address of rank `rank`'s semaphores: ARX_MAX_PAD_BLOCKS entries of
  * 32 u32 (128 bytes), flag at [0] and base at [1]; NULL if not initialised

@@ -33,6 +33,7 @@ SIGNATURES = [
     ("arx_reduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_void_p]),
     ("arx_barrier_blockwise", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
     ("arx_counter_barrier", _c.c_int, [_c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p]),
+    ("arx_symm_allreduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_size_t, _c.c_int, _c.c_void_p]),
     ("arx_sem_ptr", _c.c_void_p, [_c.c_int]),
     ("arx_epoch_ptr", _c.c_void_p, []),
     ("arx_recv_ptr", _c.c_void_p, [_c.c_int, _c.c_int]),
@@ -128,6 +129,12 @@ def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, str
 def counter_barrier(nblocks: int, rounds: int = 1, seen=None, stream=None):
     """seen: optional int32 device tensor [nblocks] receiving each block's epoch."""
     _check(lib.arx_counter_barrier(nblocks, rounds, _ptr(seen), _stream(stream)))
+
+
+def symm_allreduce(inputs, outputs, n: int, iters: int, stream=None):
+    """inputs / outputs: bf16 device tensors [iters, W, ld] (ld >= n, ld % 8 == 0)."""
+    ld = inputs.shape[-1]
+    _check(lib.arx_symm_allreduce(_ptr(inputs), _ptr(outputs), n, ld, iters, _stream(stream)))
 
 
 def sem_view(rank: int):

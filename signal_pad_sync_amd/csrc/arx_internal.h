@@ -33,6 +33,7 @@ enum : uint64_t {
   ERR_GO_TIMEOUT = 2,       // a workgroup gave up waiting for go
   ERR_BARRIER_TIMEOUT = 3,  // a signal-pad CAS wait gave up
   ERR_COUNTER_TIMEOUT = 4,  // a counter-barrier wait gave up
+  ERR_SYMM_TIMEOUT = 5,     // a barrier wait of the symmetric-buffer exchange gave up
 };
 
 // Device words (u32), each on its own 256-byte line of one allocation.
@@ -91,6 +92,21 @@ struct CounterArgs {
   Ctl* ctl;
 };
 
+struct SymmArgs {
+  const uint16_t* inputs;  // [iters][W][ld]: rank v's partial for iteration k at (k * W + v) * ld
+  uint16_t* outputs;       // [iters][W][ld]: rank v's result for iteration k
+  uint16_t* symm;          // [W][stride]: rank v's symmetric buffer at v * stride
+  uint64_t stride;
+  uint64_t ld;
+  uint32_t n;
+  int iters;
+  int blocks;              // workgroups per rank
+  int world;
+  uint32_t* pad[8];
+  uint64_t timeout;
+  Ctl* ctl;
+};
+
 // Launchers (defined in arx_kernels.hip). W in [2, 8]. block: threads per
 // one-shot workgroup (256, 512 or 1024), or 0 to choose by n.
 hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, hipStream_t stream);
@@ -98,6 +114,8 @@ int oneshot_block(uint32_t n);
 hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t stream);
 hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t stream);
 hipError_t launch_counter_barrier(const CounterArgs& a, int nblocks, hipStream_t stream);
+hipError_t launch_symm_allreduce(const SymmArgs& a, hipStream_t stream);
+int symm_blocks(uint32_t n, int world);
 hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t stream);
 
 // Grid the one-shot kernel uses for n elements with `block` threads per

@@ -38,6 +38,7 @@ struct State {
   uint32_t* pads = nullptr;   // device [W][ARX_MAX_PAD_BLOCKS][W]
   arx::Semaphore* sems = nullptr;  // device [W][ARX_MAX_PAD_BLOCKS]
   uint32_t* epochs = nullptr;      // device [ARX_MAX_PAD_BLOCKS]
+  uint16_t* symm = nullptr;        // device [W][stride]: the virtual ranks' symmetric buffers
   uint32_t* words = nullptr;  // device [WORDS_TOTAL]
   Ctl* ctl = nullptr;         // pinned, host address
   uint64_t* flags = nullptr;  // pinned, host address [8]
@@ -125,6 +126,8 @@ void free_all() {
   if (S.pads) (void)hipFree(S.pads);
   if (S.sems) (void)hipFree(S.sems);
   if (S.epochs) (void)hipFree(S.epochs);
+  if (S.symm) (void)hipFree(S.symm);
+  S.symm = nullptr;
   S.sems = nullptr;
   S.epochs = nullptr;
   if (S.words) (void)hipFree(S.words);
@@ -161,13 +164,15 @@ int init_impl(int world, size_t max_n, int rank) {
   const size_t words_b = arx::WORDS_TOTAL * sizeof(uint32_t);
   const size_t sems_b = (size_t)world * ARX_MAX_PAD_BLOCKS * sizeof(arx::Semaphore);
   const size_t epochs_b = ARX_MAX_PAD_BLOCKS * sizeof(uint32_t);
+  const size_t symm_b = (size_t)world * S.stride * sizeof(uint16_t);
   int rc = ARX_OK;
   hipError_t e;
   if ((e = hipMalloc(&S.send, send_b)) != hipSuccess || (e = hipMalloc(&S.recv, recv_b)) != hipSuccess ||
       (e = hipMalloc(&S.pads, pads_b)) != hipSuccess || (e = hipMalloc(&S.words, words_b)) != hipSuccess ||
-      (e = hipMalloc(&S.sems, sems_b)) != hipSuccess || (e = hipMalloc(&S.epochs, epochs_b)) != hipSuccess) {
+      (e = hipMalloc(&S.sems, sems_b)) != hipSuccess || (e = hipMalloc(&S.epochs, epochs_b)) != hipSuccess ||
+      (e = hipMalloc(&S.symm, symm_b)) != hipSuccess) {
     rc = fail(ARX_ENOMEM, "device allocation of %zu bytes failed: %s",
-              send_b + recv_b + pads_b + words_b + sems_b + epochs_b, hipGetErrorString(e));
+              send_b + recv_b + pads_b + words_b + sems_b + epochs_b + symm_b, hipGetErrorString(e));
   } else if ((e = hipHostMalloc((void**)&S.ctl, 4096, hipHostMallocCoherent | hipHostMallocMapped)) !=
                  hipSuccess ||
              (e = hipHostMalloc((void**)&S.flags, 4096, hipHostMallocCoherent | hipHostMallocMapped)) !=
@@ -308,6 +313,33 @@ int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t str
   a.timeout = timeout_ticks();
   a.ctl = S.ctl_dev;
   HIPCHK(arx::launch_counter_barrier(a, nblocks, stream));
+  return ARX_OK;
+}
+
+int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, int iters, hipStream_t stream) {
+  int rc = check_ready();
+  if (rc != ARX_OK) return rc;
+  if (n > S.max_n) return fail(ARX_EINVAL, "n %zu exceeds max_n %zu", n, S.max_n);
+  if (ld < n || (ld & 7u)) return fail(ARX_EINVAL, "ld %zu must be >= n and a multiple of 8", ld);
+  if (iters < 1 || iters > 65536) return fail(ARX_EINVAL, "iters %d not in [1, 65536]", iters);
+  if (n > 0 && (inputs == nullptr || outputs == nullptr)) return fail(ARX_EINVAL, "null inputs or outputs");
+  if (((uintptr_t)inputs & 15u) || ((uintptr_t)outputs & 15u))
+    return fail(ARX_EINVAL, "inputs and outputs must be 16-byte aligned");
+  arx::SymmArgs a;
+  a.inputs = (const uint16_t*)inputs;
+  a.outputs = (uint16_t*)outputs;
+  a.symm = S.symm;
+  a.stride = S.stride;
+  a.ld = ld;
+  a.n = (uint32_t)n;
+  a.iters = iters;
+  a.world = S.world;
+  a.blocks = arx::symm_blocks(a.n, S.world);
+  for (int i = 0; i < 8; ++i)
+    a.pad[i] = i < S.world ? S.pads + (size_t)i * ARX_MAX_PAD_BLOCKS * S.world : nullptr;
+  a.timeout = timeout_ticks();
+  a.ctl = S.ctl_dev;
+  HIPCHK(arx::launch_symm_allreduce(a, stream));
   return ARX_OK;
 }
 
