@@ -39,7 +39,7 @@ def recorded_traffic(key):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256()
-    for f in ("arx_kernels.hip", "arx_device.h", "arx_internal.h"):
+    for f in ("arx_reduce.hip", "arx_kernel_util.h", "arx_device.h", "arx_internal.h"):
         with open(os.path.join(ROOT, "signal_pad_sync_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return rec.get(key) if rec.get("kernel_source_sha256") == h.hexdigest() else None

@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libarx.so")
-SOURCES = [os.path.join(CSRC, "arx_kernels.hip"), os.path.join(CSRC, "arx_runtime.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("arx_reduce.hip", "arx_sync.hip", "arx_runtime.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

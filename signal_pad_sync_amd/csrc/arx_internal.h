@@ -107,7 +107,7 @@ struct SymmArgs {
   Ctl* ctl;
 };
 
-// Launchers (defined in arx_kernels.hip). W in [2, 8]. block: threads per
+// Launchers (defined in arx_reduce.hip and arx_sync.hip). W in [2, 8]. block: threads per
 // one-shot workgroup (256, 512 or 1024), or 0 to choose by n.
 hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, hipStream_t stream);
 int oneshot_block(uint32_t n);

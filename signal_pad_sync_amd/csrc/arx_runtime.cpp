@@ -17,8 +17,8 @@
 #include <thread>
 
 #include "arx.h"
-#include "arx_device.h"
 #include "arx_internal.h"
+#include "arx_sync.h"
 #include "arx_proxy.h"
 
 namespace {
