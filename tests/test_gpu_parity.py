@@ -339,3 +339,49 @@ def test_counter_barrier_flags_bases_epochs(W):
                 assert np.array_equal(sem[:, 1], 2 * W * rounds_done), f"bases of rank {r}"
             assert np.array_equal(arx.epoch_view().cpu().numpy(), launches % 2)
             assert arx.debug_state()["ctl_err"] == 0
+
+
+@pytest.mark.parametrize("W", [2, 3, 4, 5, 6, 7])
+def test_reduce_only_every_world(W):
+    """The reduction alone at every W below 8, with this GPU at the last rank
+    and ragged tails, both parities."""
+    rank = W - 1
+    max_n = 300007
+    recv = [[WL.uniform(15000 + 10 * par + s, max_n) for s in range(W)] for par in (0, 1)]
+    with library(W, max_n, rank=rank):
+        fill_recv(recv, rank)
+        for n in (1, 9, 2048 + 3, 300007):
+            for par in (0, 1):
+                x = WL.uniform(16000 + n + par, n)
+                inp, out = to_dev(x, pad_to=max_n + 1), sentinel(max_n + 1)
+                note(f"reduce-only W={W} n={n} par={par}")
+                arx.reduce(inp, out, par, n)
+                torch.cuda.synchronize()
+                parts = [x if s == rank else recv[par][s] for s in range(W)]
+                got = to_host(out)
+                assert_bits(got[:n], R.reduce(parts, n=n), f"reduce-only W={W} n={n} par={par}")
+                assert np.all(got[n:] == 0xDEAD)
+
+
+def test_counter_barrier_graph_replays():
+    """The counter barrier captured in a hipGraph, replayed with eager launches
+    between replays: flags and bases keep following 2 * W * rounds."""
+    W = 4
+    with library(W, 1024):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            arx.counter_barrier(256, 2)
+        total = 0
+        for rep in range(5):
+            note(f"counter barrier graph replay {rep}")
+            g.replay()
+            total += 2
+            if rep % 2:
+                arx.counter_barrier(256, 1)
+                total += 1
+            torch.cuda.synchronize()
+            for r in range(W):
+                sem = arx.sem_view(r).cpu().numpy()
+                assert np.all(sem[:256, 0] == 2 * W * total) and np.all(sem[:256, 1] == 2 * W * total)
+                assert np.all(sem[256:, 0] == 0)
+            assert arx.debug_state()["ctl_err"] == 0
