@@ -236,9 +236,18 @@ int arx_status(uint64_t* published, uint64_t* posted, uint64_t* done);
  * device), into words[0..nwords): [0] seq_dev, [1] arrival counter,
  * [2] finish counter, [3] go, [4] abort, [5] ctl.seq, [6] ctl.bytes[0],
  * [7] ctl.bytes[1], [8] ctl.done, [9] ctl.err, [10] ctl.err_seq,
- * [11] posted, [12 .. 12+W) flags[src]. Returns the number of words written.
+ * [11] posted, [12 .. 12+W) flags[src]. seq_dev, ctl.seq, ctl.done, posted
+ * abort and the flags are 64-bit sequence numbers; go holds the low 32 bits
+ * of one. Returns the number of words written.
  */
 int arx_debug_state(uint64_t* words, int nwords);
+
+/* Test aid: set the protocol's state as if `seq` calls had completed
+ * (device seq and go, ctl.seq, ctl.done, the proxy's posted seq and every
+ * peer flag), so tests can reach large sequence numbers. Waits for the
+ * device; allowed in the lockstep and manual modes only, with no call in
+ * flight. Errors: ARX_ESTATE, ARX_EHIP. */
+int arx_debug_set_seq(uint64_t seq);
 
 /* The binary32 -> bf16 rounding of the reduction alone (for exhaustive
  * checks): out[i] = the bf16 pattern the reduction writes for the binary32

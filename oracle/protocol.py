@@ -76,9 +76,9 @@ class ProtocolState:
     """Every protocol word of one rank (page "arx.cu": struct Ctl, struct Dev)."""
     W: int
     rank: int
-    seq_dev: int = 0            # device u32: last completed seq
+    seq_dev: int = 0            # device u64: last completed seq
     cnt: List[int] = field(default_factory=lambda: [0, 0])  # arrival / finish counters
-    go: int = 0                 # device u32: seq whose peer data has all arrived
+    go: int = 0                 # device u32: low 32 bits of the seq whose peer data has all arrived
     ctl_seq: int = 0            # pinned u64: last published seq
     ctl_bytes: List[int] = field(default_factory=lambda: [0, 0])  # bytes per parity
     ctl_done: int = 0           # pinned u64: last seq summed
@@ -118,11 +118,11 @@ def sequential_model(calls: Sequence[Tuple[np.ndarray, int]], recv, W: int, rank
     st = state or ProtocolState(W=W, rank=rank)
     if st.send is None:
         st.send = [np.zeros(max_n, np.uint16), np.zeros(max_n, np.uint16)]
-    if mode == RUNAHEAD and st.posted == 0:
-        _post(st, 1)                       # seq 1 needs only seq 0, published at init
+    if mode == RUNAHEAD and st.posted == st.ctl_seq:
+        _post(st, st.ctl_seq + 1)          # the next seq needs only the last published one
     outs = []
     for x, n in calls:
-        seq = (st.seq_dev + 1) & U32       # seq_dev is a device u32
+        seq = st.seq_dev + 1
         par = seq & 1
         st.send[par][:n] = np.asarray(x, dtype=np.uint16)[:n]       # copy into the send slot
         st.ctl_bytes[par] = 2 * n
@@ -133,7 +133,7 @@ def sequential_model(calls: Sequence[Tuple[np.ndarray, int]], recv, W: int, rank
             _post(st, seq + 1)
         if any(st.flags[src] < seq for src in range(W) if src != rank):
             raise RuntimeError(f"seq {seq}: a peer flag never reached seq (flags {st.flags})")
-        st.go = seq                        # workgroup 0 releases the others
+        st.go = seq & U32                  # workgroup 0 releases the others
         parts = [st.send[par] if src == rank else recv[par][src] for src in range(W)]
         outs.append(_reduce.reduce(parts, n=n))
         st.seq_dev = seq                   # last block out

@@ -44,6 +44,7 @@ SIGNATURES = [
     ("arx_set_timeout_us", _c.c_int, [_c.c_uint64]),
     ("arx_status", _c.c_int, [_u64p, _u64p, _u64p]),
     ("arx_debug_state", _c.c_int, [_u64p, _c.c_int]),
+    ("arx_debug_set_seq", _c.c_int, [_c.c_uint64]),
     ("arx_test_round_bf16", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     ("arx_strerror", _c.c_char_p, [_c.c_int]),
     ("arx_max_n", _c.c_size_t, []),
@@ -173,6 +174,10 @@ def debug_state() -> dict:
     d = {name: buf[i] for i, name in enumerate(STATE_WORDS)}
     d["flags"] = [buf[i] for i in range(len(STATE_WORDS), m)]
     return d
+
+
+def debug_set_seq(seq: int):
+    _check(lib.arx_debug_set_seq(seq))
 
 
 def max_n() -> int:

@@ -38,11 +38,11 @@ enum : uint64_t {
 
 // Device words (u32), each on its own 256-byte line of one allocation.
 enum : int {
-  WORD_SEQ = 0,      // last completed seq
+  WORD_SEQ = 0,      // last completed seq (u64: words 0 and 1)
   WORD_CNT0 = 64,    // workgroups past the copy (arrival counter)
   WORD_CNT1 = 128,   // workgroups finished (finish counter)
   WORD_GO = 192,     // seq whose peer data has all arrived
-  WORD_ABORT = 256,  // seq whose wait timed out (its reduction is skipped)
+  WORD_ABORT = 256,  // seq whose wait timed out, its reduction skipped (u64: words 256 and 257)
   WORDS_TOTAL = 1024,
 };
 

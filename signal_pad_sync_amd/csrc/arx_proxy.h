@@ -52,6 +52,15 @@ class Proxy {
     return publish_locked(s);
   }
 
+  // Sets the posted seq and every peer flag to s, as if seqs 1..s had been
+  // posted (state set-up for tests; no call may be in flight).
+  void reset(uint64_t s) {
+    std::lock_guard<std::mutex> g(mu_);
+    for (int src = 0; src < world_; ++src)
+      if (src != rank_) __atomic_store_n(&flags_[src], s, __ATOMIC_RELEASE);
+    posted_.store(s, std::memory_order_release);
+  }
+
   // One pass of the loop: post up to the seq the mode allows (in stress
   // mode each post is preceded by before_post), or else run the watchdog
   // check. Returns false if posting failed: before_post failed, or an order

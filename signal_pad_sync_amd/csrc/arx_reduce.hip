@@ -27,15 +27,19 @@ namespace arx {
 template <int W, bool ONE_PASS, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   __shared__ uint32_t s_abort;
-  uint32_t* const seq_dev = a.words + WORD_SEQ;
+  uint64_t* const seq_dev = reinterpret_cast<uint64_t*>(a.words + WORD_SEQ);
   uint32_t* const cnt0 = a.words + WORD_CNT0;
   uint32_t* const cnt1 = a.words + WORD_CNT1;
   uint32_t* const go = a.words + WORD_GO;
-  uint32_t* const abort_w = a.words + WORD_ABORT;
+  uint64_t* const abort_w = reinterpret_cast<uint64_t*>(a.words + WORD_ABORT);
 
-  // seq and parity: one more than the last completed call
-  const uint32_t seq = load_relaxed_agent(seq_dev) + 1u;
-  const uint32_t par = seq & 1u;
+  // seq and parity: one more than the last completed call. seq is 64-bit
+  // like the host's flags; go holds its low 32 bits (compared by signed
+  // difference), abort all 64 (a call's abort must never match the zero the
+  // word starts at, which a low half of 0 at seq 2^32 would).
+  const uint64_t seq = load_relaxed_agent(seq_dev) + 1u;
+  const uint32_t seq32 = (uint32_t)seq;
+  const uint32_t par = seq32 & 1u;
   uint16_t* const mine = a.send + (size_t)par * a.stride;
   const uint32_t nv = a.n >> 3, tail = a.n & 7u;
   const uint32_t tid = blockIdx.x * BLOCK + threadIdx.x;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
       fence_acquire_system();
       store_relaxed_agent(cnt0, 0u);
       store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
-      store_release_system(&a.ctl->seq, (uint64_t)seq);
+      store_release_system(&a.ctl->seq, seq);
     }
   }
 
@@ -75,7 +79,7 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
     bool ok = true;
     if ((int)threadIdx.x < W && (int)threadIdx.x != a.rank) {
       const uint64_t t0 = now_ticks();
-      while (load_relaxed_system(a.flags + threadIdx.x) < (uint64_t)seq) {
+      while (load_relaxed_system(a.flags + threadIdx.x) < seq) {
         if (now_ticks() - t0 > a.timeout) {
           ok = false;
           break;
@@ -83,21 +87,22 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    fence_acquire_system();
+    // the polling wave acquires; the workgroup barrier orders the others
+    if (threadIdx.x < 64) fence_acquire_system();
     const int bad = __syncthreads_or(!ok);
     if (threadIdx.x == 0) {
       if (bad) {
         store_relaxed_agent(abort_w, seq);
         report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
       }
-      store_release_agent(go, seq);
+      store_release_agent(go, seq32);
     }
     abort = bad != 0;
   } else {
     if (threadIdx.x == 0) {
       const uint64_t t0 = now_ticks();
       bool timed = false;
-      while ((int32_t)(load_relaxed_agent(go) - seq) < 0) {
+      while ((int32_t)(load_relaxed_agent(go) - seq32) < 0) {
         if (now_ticks() - t0 > 2u * a.timeout) {
           timed = true;
           break;
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
     if (fetch_add_relaxed_agent(cnt1, 1u) == gridDim.x - 1u) {
       store_relaxed_agent(cnt1, 0u);
       store_relaxed_agent(seq_dev, seq);
-      store_relaxed_system(&a.ctl->done, (uint64_t)seq);
+      store_relaxed_system(&a.ctl->done, seq);
     }
   }
 }

@@ -414,11 +414,11 @@ int arx_debug_state(uint64_t* words, int nwords) {
   uint32_t dw[arx::WORDS_TOTAL];
   HIPCHK(hipMemcpy(dw, S.words, sizeof dw, hipMemcpyDeviceToHost));
   uint64_t all[12 + ARX_MAX_WORLD];
-  all[0] = dw[arx::WORD_SEQ];
+  all[0] = dw[arx::WORD_SEQ] | (uint64_t)dw[arx::WORD_SEQ + 1] << 32;
   all[1] = dw[arx::WORD_CNT0];
   all[2] = dw[arx::WORD_CNT1];
   all[3] = dw[arx::WORD_GO];
-  all[4] = dw[arx::WORD_ABORT];
+  all[4] = dw[arx::WORD_ABORT] | (uint64_t)dw[arx::WORD_ABORT + 1] << 32;
   all[5] = load_acquire(&S.ctl->seq);
   all[6] = load_acquire(&S.ctl->bytes[0]);
   all[7] = load_acquire(&S.ctl->bytes[1]);
@@ -431,6 +431,21 @@ int arx_debug_state(uint64_t* words, int nwords) {
   const int m = nwords < total ? nwords : total;
   for (int i = 0; i < m; ++i) words[i] = all[i];
   return m;
+}
+
+int arx_debug_set_seq(uint64_t seq) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  const int mode = S.core->mode.load();
+  if (mode != ARX_PROXY_LOCKSTEP && mode != ARX_PROXY_MANUAL)
+    return fail(ARX_ESTATE, "set the seq in lockstep or manual mode");
+  HIPCHK(hipDeviceSynchronize());
+  uint32_t w[2] = {(uint32_t)seq, (uint32_t)(seq >> 32)};
+  HIPCHK(hipMemcpy(S.words + arx::WORD_SEQ, w, sizeof w, hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(S.words + arx::WORD_GO, w, sizeof(uint32_t), hipMemcpyHostToDevice));
+  store_release(&S.ctl->done, seq);
+  store_release(&S.ctl->seq, seq);
+  S.core->reset(seq);
+  return ARX_OK;
 }
 
 int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream) {

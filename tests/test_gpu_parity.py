@@ -385,3 +385,28 @@ def test_counter_barrier_graph_replays():
                 assert np.all(sem[:256, 0] == 2 * W * total) and np.all(sem[:256, 1] == 2 * W * total)
                 assert np.all(sem[256:, 0] == 0)
             assert arx.debug_state()["ctl_err"] == 0
+
+
+@pytest.mark.parametrize("mode", [arx.PROXY_LOCKSTEP, arx.PROXY_RUNAHEAD])
+def test_seq_crosses_32_bits(mode):
+    """Sequence numbers past 2^32: the device seq is 64-bit like the flags,
+    go's low 32 bits wrap, parity keeps alternating, every call bit-exact."""
+    W, n, start = 4, 8192 + 3, (1 << 32) - 3
+    recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
+    xs = [WL.uniform(18000 + k, n) for k in range(8)]
+    with library(W, n):
+        fill_recv(recv, 0)
+        arx.debug_set_seq(start)
+        arx.set_proxy_mode(mode)
+        st = P.ProtocolState(W=W, rank=0, seq_dev=start, go=start & 0xFFFFFFFF, ctl_seq=start, ctl_done=start,
+                             flags=[0] + [start] * (W - 1), posted=start)
+        for k, x in enumerate(xs):
+            inp, out = to_dev(x, pad_to=n + 5), sentinel(n + 5)
+            note(f"seq {start + k + 1}, mode {mode}")
+            arx.allreduce(inp, out, n)
+            torch.cuda.synchronize()
+            st, outs = P.sequential_model([(x, n)], recv, W, mode=P.RUNAHEAD if mode == arx.PROXY_RUNAHEAD else
+                                          P.LOCKSTEP, max_n=n, state=st)
+            assert_bits(to_host(out)[:n], outs[0], f"seq {start + k + 1}")
+        check_state(st, 0, wait_posted=st.posted)
+        assert st.seq_dev == start + len(xs) > (1 << 32)
