@@ -57,7 +57,8 @@ def parse():
     ap.add_argument("--reduce-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,graph,reduce,barrier,symm")
+    ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,graph,reduce,barrier,symm; "
+                    "configs (every workload, oracle included) runs only when named")
     return ap.parse_args()
 
 
@@ -220,6 +221,102 @@ def bench_symm(args):
     return us / iters
 
 
+def _oracle_times(parts, n, reps=3):
+    """Median seconds of the oracle's reduction over n elements, on one
+    thread and on every host core this process may use."""
+    from oracle import reduce as R
+    T = len(os.sched_getaffinity(0))
+    out = {}
+    for name, threads in (("1", 1), ("T", T)):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            R.reduce(parts, n=n, threads=threads)
+            ts.append(time.perf_counter() - t0)
+        out[name] = sorted(ts)[len(ts) // 2]
+    return out, T
+
+
+def bench_configs(args):
+    """Every workload once more, as a table: GPU time per call (or per
+    launch / graph replay) and the oracle's time on 1 and T host threads."""
+    import numpy as np
+    import torch
+    from signal_pad_sync_amd import arx
+    from signal_pad_sync_amd import workloads as WL
+
+    rows = {}
+    stream = torch.cuda.current_stream()
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def fill(recv, W, rank=0):
+        for par in (0, 1):
+            for src in range(W):
+                if src != rank:
+                    arx.recv_view(par, src, recv[par][src].size).copy_(dev(recv[par][src]))
+
+    # workloads 1, 2 and 5: consecutive eager one-shot calls, lockstep proxy
+    for cfg, n_buf in ((1, 8192), (2, 131072), (5, 131072)):
+        w = WL.WORKLOADS[cfg]
+        W, n = w["W"], w["n"]
+        recv = [WL.recv_partials(cfg, par, n) for par in (0, 1)]
+        arx.init(W, n_buf)
+        try:
+            fill(recv, W)
+            x = torch.zeros(n_buf, dtype=torch.bfloat16, device="cuda")
+            x[:n].copy_(dev(recv[1][0]))
+            out = torch.empty_like(x)
+            call, xp, op, sh = arx.lib.arx_allreduce, x.data_ptr(), out.data_ptr(), stream.cuda_stream
+            for _ in range(20):
+                call(xp, op, n, sh)
+            us = timed(lambda: call(xp, op, n, sh), args.steps, stream) / args.steps
+            assert arx.debug_state()["ctl_err"] == 0
+        finally:
+            torch.cuda.synchronize()
+            arx.finalize()
+        cpu, T = _oracle_times(recv[1], n)
+        rows[f"workload{cfg}"] = {"W": W, "n": n, "gpu_us_per_call": round(us, 3),
+                                  "gpu_GBps": round((W + 3) * 2 * n / us / 1e3, 1),
+                                  "oracle_ms_1thread": round(cpu["1"] * 1e3, 3),
+                                  "oracle_ms_Tthreads": round(cpu["T"] * 1e3, 3), "T": T}
+    # workload 3: one-shot call + 256-workgroup barrier in one hipGraph, per n
+    W = 4
+    for n in WL.WORKLOADS[3]["ns"]:
+        recv = [WL.recv_partials(3, par, n) for par in (0, 1)]
+        arx.init(W, n)
+        try:
+            fill(recv, W)
+            x = dev(WL.own_partial(3, 1, n))
+            out = torch.empty_like(x)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(10):
+                    arx.allreduce(x, out, n)
+                    arx.barrier_blockwise(256, arx.SEM_ACQ_REL, 1)
+            for _ in range(3):
+                g.replay()
+            reps = max(1, args.steps // 10)
+            us = timed(g.replay, reps, stream) / (reps * 10)
+            assert arx.debug_state()["ctl_err"] == 0
+        finally:
+            torch.cuda.synchronize()
+            arx.finalize()
+        cpu, T = _oracle_times(recv[1], n)
+        rows[f"workload3_n{n}"] = {"W": W, "n": n, "gpu_us_per_call_and_barrier": round(us, 3),
+                                   "oracle_ms_1thread": round(cpu["1"] * 1e3, 4),
+                                   "oracle_ms_Tthreads": round(cpu["T"] * 1e3, 4), "T": T}
+    # workload 4: the oracle on the full size (the GPU figure is the reduce phase)
+    n = 8192 * 8192
+    parts = WL.recv_partials(4, 0, n)
+    cpu, T = _oracle_times(parts, n, reps=1)
+    rows["workload4"] = {"W": 8, "n": n, "oracle_ms_1thread": round(cpu["1"] * 1e3, 1),
+                         "oracle_ms_Tthreads": round(cpu["T"] * 1e3, 1), "T": T,
+                         "oracle_GBps_Tthreads": round(9 * 2 * n / cpu["T"] / 1e9, 2)}
+    return rows
+
+
 def cpu_baseline(seconds):
     """The oracle's one-shot model (sequential protocol + C reduction) on the
     headline workload, single-threaded, for about `seconds` of CPU time."""
@@ -294,6 +391,11 @@ def main():
             extra[f"barrier_256wg_{name}_us"] = round(us_b, 3)
             log(f"  {us_b:.3f} us/launch")
 
+    if args.only and "configs" in only:
+        log("every workload: GPU time and oracle time on 1 and T threads")
+        extra["configs"] = bench_configs(args)
+        for k, v in extra["configs"].items():
+            log(f"  {k}: {v}")
     if want("symm"):
         log("symmetric-buffer all-reduce among 8 virtual ranks, n=131072, 100 iterations per launch")
         us_s = bench_symm(args)
