@@ -108,19 +108,21 @@ struct SymmArgs {
 };
 
 // Launchers (defined in arx_reduce.hip and arx_sync.hip). W in [2, 8]. block: threads per
-// one-shot workgroup (256, 512 or 1024), or 0 to choose by n.
-hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, hipStream_t stream);
+// one-shot workgroup (256, 512 or 1024), or 0 to choose by n. cus: compute
+// units of the device; kernels whose workgroups wait on each other keep
+// their grid within what is resident at once.
+hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, int cus, hipStream_t stream);
 int oneshot_block(uint32_t n);
 hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t stream);
 hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t stream);
 hipError_t launch_counter_barrier(const CounterArgs& a, int nblocks, hipStream_t stream);
 hipError_t launch_symm_allreduce(const SymmArgs& a, hipStream_t stream);
-int symm_blocks(uint32_t n, int world);
+int symm_blocks(uint32_t n, int world, int cus);
 hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t stream);
 
 // Grid the one-shot kernel uses for n elements with `block` threads per
-// workgroup (all its workgroups must be resident at once, since they wait
-// on each other).
-unsigned oneshot_grid(uint32_t n, int block);
+// workgroup, at most max_grid (all its workgroups must be resident at once,
+// since they wait on each other).
+unsigned oneshot_grid(uint32_t n, int block, unsigned max_grid);
 
 }  // namespace arx

@@ -164,17 +164,38 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   }
 }
 
-unsigned oneshot_grid(uint32_t n, int block) {
+unsigned oneshot_grid(uint32_t n, int block, unsigned max_grid) {
   const uint32_t nv = n >> 3;
   uint32_t g = (nv + block - 1) / block;
   if (g < 1) g = 1;
-  if (g > (uint32_t)kMaxOneShotGrid) g = kMaxOneShotGrid;
+  if (g > max_grid) g = max_grid;
   return g;
 }
 
+// Workgroups of oneshot_kernel<W, ONE_PASS, BLOCK> that fit on the device at
+// once: its occupancy per CU times the CU count, at most kMaxOneShotGrid; 0
+// if the occupancy query fails. The occupancy is queried once per variant.
+template <int W, bool ONE_PASS, int BLOCK>
+static unsigned coresident(int cus) {
+  static const int per_cu = [] {
+    int o = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+               &o, reinterpret_cast<const void*>(oneshot_kernel<W, ONE_PASS, BLOCK>), BLOCK, 0) == hipSuccess
+               ? o
+               : 0;
+  }();
+  const long long cap = (long long)per_cu * cus;
+  return (unsigned)(cap < kMaxOneShotGrid ? cap : kMaxOneShotGrid);
+}
+
 template <int W, int BLOCK>
-static hipError_t launch_oneshot_wb(const OneShotArgs& a, hipStream_t s) {
-  const unsigned grid = oneshot_grid(a.n, BLOCK);
+static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s) {
+  // every workgroup waits on the others, so all must be resident together
+  const unsigned cap = coresident<W, false, BLOCK>(cus);
+  const unsigned cap1 = coresident<W, true, BLOCK>(cus);
+  const unsigned max_grid = cap < cap1 ? cap : cap1;
+  if (max_grid == 0) return hipErrorInvalidConfiguration;
+  const unsigned grid = oneshot_grid(a.n, BLOCK, max_grid);
   const bool one_pass = (a.n >> 3) <= grid * (uint32_t)BLOCK;
   if (one_pass)
     hipLaunchKernelGGL((oneshot_kernel<W, true, BLOCK>), dim3(grid), dim3(BLOCK), 0, s, a);
@@ -196,25 +217,25 @@ int oneshot_block(uint32_t n) {
 }
 
 template <int W>
-static hipError_t launch_oneshot_w(const OneShotArgs& a, int block, hipStream_t s) {
+static hipError_t launch_oneshot_w(const OneShotArgs& a, int block, int cus, hipStream_t s) {
   if (block == 0) block = oneshot_block(a.n);
   switch (block) {
-    case 256: return launch_oneshot_wb<W, 256>(a, s);
-    case 512: return launch_oneshot_wb<W, 512>(a, s);
-    case 1024: return launch_oneshot_wb<W, 1024>(a, s);
+    case 256: return launch_oneshot_wb<W, 256>(a, cus, s);
+    case 512: return launch_oneshot_wb<W, 512>(a, cus, s);
+    case 1024: return launch_oneshot_wb<W, 1024>(a, cus, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, hipStream_t s) {
+hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, int cus, hipStream_t s) {
   switch (W) {
-    case 2: return launch_oneshot_w<2>(a, block, s);
-    case 3: return launch_oneshot_w<3>(a, block, s);
-    case 4: return launch_oneshot_w<4>(a, block, s);
-    case 5: return launch_oneshot_w<5>(a, block, s);
-    case 6: return launch_oneshot_w<6>(a, block, s);
-    case 7: return launch_oneshot_w<7>(a, block, s);
-    case 8: return launch_oneshot_w<8>(a, block, s);
+    case 2: return launch_oneshot_w<2>(a, block, cus, s);
+    case 3: return launch_oneshot_w<3>(a, block, cus, s);
+    case 4: return launch_oneshot_w<4>(a, block, cus, s);
+    case 5: return launch_oneshot_w<5>(a, block, cus, s);
+    case 6: return launch_oneshot_w<6>(a, block, cus, s);
+    case 7: return launch_oneshot_w<7>(a, block, cus, s);
+    case 8: return launch_oneshot_w<8>(a, block, cus, s);
     default: return hipErrorInvalidValue;
   }
 }

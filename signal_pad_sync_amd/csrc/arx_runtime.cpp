@@ -31,7 +31,7 @@ static_assert(ARX_PROXY_LOCKSTEP == arx::PROXY_LOCKSTEP && ARX_PROXY_RUNAHEAD ==
 
 struct State {
   bool inited = false;
-  int world = 0, rank = 0, device = 0;
+  int world = 0, rank = 0, device = 0, cus = 0;
   size_t max_n = 0, stride = 0;
   uint16_t* send = nullptr;   // device [2][stride]
   uint16_t* recv = nullptr;   // device [2][W][stride]
@@ -157,6 +157,7 @@ int init_impl(int world, size_t max_n, int rank) {
   int khz = 0;
   HIPCHK(hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, S.device));
   S.clock_khz = khz > 0 ? (uint64_t)khz : 100000;
+  HIPCHK(hipDeviceGetAttribute(&S.cus, hipDeviceAttributeMultiprocessorCount, S.device));
 
   const size_t send_b = 2 * S.stride * sizeof(uint16_t);
   const size_t recv_b = 2 * (size_t)world * S.stride * sizeof(uint16_t);
@@ -258,7 +259,7 @@ int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream) {
   a.n = (uint32_t)n;
   a.rank = S.rank;
   a.timeout = timeout_ticks();
-  HIPCHK(arx::launch_oneshot(a, S.world, 0, stream));
+  HIPCHK(arx::launch_oneshot(a, S.world, 0, S.cus, stream));
   return ARX_OK;
 }
 
@@ -334,7 +335,7 @@ int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, i
   a.n = (uint32_t)n;
   a.iters = iters;
   a.world = S.world;
-  a.blocks = arx::symm_blocks(a.n, S.world);
+  a.blocks = arx::symm_blocks(a.n, S.world, S.cus);
   for (int i = 0; i < 8; ++i)
     a.pad[i] = i < S.world ? S.pads + (size_t)i * ARX_MAX_PAD_BLOCKS * S.world : nullptr;
   a.timeout = timeout_ticks();

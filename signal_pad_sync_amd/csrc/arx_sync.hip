@@ -151,15 +151,38 @@ fail:
   if (threadIdx.x == 0) report_error(a.ctl, ERR_SYMM_TIMEOUT, (uint64_t)blockIdx.x);
 }
 
-// Workgroups per rank: about two vectors per thread, at most 64 per rank so
-// that all W * blocks workgroups are resident together.
-int symm_blocks(uint32_t n, int world) {
-  (void)world;
+// Workgroups per rank: about two vectors per thread, at most 64 per rank,
+// and few enough that all W * blocks workgroups are resident together
+// (occupancy per CU times the CU count, queried once per W).
+template <int W>
+static int symm_blocks_w(uint32_t n, int cus) {
+  static const int per_cu = [] {
+    int o = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+               &o, reinterpret_cast<const void*>(symm_allreduce_kernel<W>), kBlock, 0) == hipSuccess
+               ? o
+               : 0;
+  }();
   const uint32_t nv = n >> 3;
-  uint32_t g = (nv + 2 * kBlock - 1) / (2 * kBlock);
+  long long g = (nv + 2 * kBlock - 1) / (2 * kBlock);
   if (g < 1) g = 1;
   if (g > 64) g = 64;
+  const long long cap = (long long)per_cu * cus / W;
+  if (g > cap) g = cap;
   return (int)g;
+}
+
+int symm_blocks(uint32_t n, int world, int cus) {
+  switch (world) {
+    case 2: return symm_blocks_w<2>(n, cus);
+    case 3: return symm_blocks_w<3>(n, cus);
+    case 4: return symm_blocks_w<4>(n, cus);
+    case 5: return symm_blocks_w<5>(n, cus);
+    case 6: return symm_blocks_w<6>(n, cus);
+    case 7: return symm_blocks_w<7>(n, cus);
+    case 8: return symm_blocks_w<8>(n, cus);
+    default: return 0;
+  }
 }
 
 template <int W>
@@ -169,6 +192,7 @@ static hipError_t launch_symm_w(const SymmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_symm_allreduce(const SymmArgs& a, hipStream_t s) {
+  if (a.blocks < 1) return hipErrorInvalidConfiguration;
   switch (a.world) {
     case 2: return launch_symm_w<2>(a, s);
     case 3: return launch_symm_w<3>(a, s);
