@@ -52,6 +52,14 @@ class Proxy {
     return publish_locked(s);
   }
 
+  // Runs f while no post is in progress (posts hold the same lock), e.g. to
+  // replace what before_post reads.
+  template <typename F>
+  void locked(F&& f) {
+    std::lock_guard<std::mutex> g(mu_);
+    f();
+  }
+
   // Sets the posted seq and every peer flag to s, as if seqs 1..s had been
   // posted (state set-up for tests; no call may be in flight).
   void reset(uint64_t s) {
@@ -62,13 +70,15 @@ class Proxy {
   }
 
   // One pass of the loop: post up to the seq the mode allows (in stress
-  // mode each post is preceded by before_post), or else run the watchdog
-  // check. Returns false if posting failed: before_post failed, or an order
+  // mode each post is preceded by before_post; the mode is read again under
+  // the lock for each post, so once the mode has left stress mode and a
+  // locked() call has returned, before_post is not running and is not
+  // called again), or else run the watchdog check. Returns false if posting failed: before_post failed, or an order
   // error, which cannot happen unless publish() was also called
   // concurrently in a posting mode.
   bool step() {
     const uint64_t pub = __atomic_load_n(pub_, __ATOMIC_ACQUIRE);
-    const int m = mode.load(std::memory_order_relaxed);
+    const int m = mode.load(std::memory_order_acquire);
     const uint64_t have = posted();
     uint64_t target = have;
     if (m == PROXY_LOCKSTEP || m == PROXY_STRESS) target = pub;
@@ -76,7 +86,7 @@ class Proxy {
     if (target > have) {
       std::lock_guard<std::mutex> g(mu_);
       for (uint64_t s = posted() + 1; s <= target; ++s) {
-        if (m == PROXY_STRESS && before_post && !before_post(s)) return false;
+        if (mode.load(std::memory_order_acquire) == PROXY_STRESS && before_post && !before_post(s)) return false;
         if (!publish_locked(s)) return false;
       }
       return true;

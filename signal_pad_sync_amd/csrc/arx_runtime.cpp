@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <exception>
 #include <mutex>
 #include <memory>
 #include <thread>
@@ -196,10 +197,17 @@ int init_impl(int world, size_t max_n, int rank) {
   memset((void*)S.flags, 0, 4096);
   S.proxy_err.store(false);
   S.stop.store(false);
-  S.core.reset(new arx::Proxy(&S.ctl->seq, &S.ctl->done, S.flags, S.world, S.rank));
-  S.core->before_post = stress_copy;
   S.timeout_us = 2000000;
-  S.proxy = std::thread(proxy_main);
+  // no C++ exception may leave the C ABI
+  try {
+    S.core.reset(new arx::Proxy(&S.ctl->seq, &S.ctl->done, S.flags, S.world, S.rank));
+    S.core->before_post = stress_copy;
+    S.proxy = std::thread(proxy_main);
+  } catch (const std::exception& ex) {
+    S.core.reset();
+    free_all();
+    return fail(ARX_ENOMEM, "starting the proxy thread failed: %s", ex.what());
+  }
   S.inited = true;
   return ARX_OK;
 }
@@ -380,15 +388,15 @@ int arx_set_proxy_mode(int mode) {
 int arx_set_stress_source(const void* pool, int sets) {
   if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
   if (S.core->mode.load() == ARX_PROXY_STRESS) return fail(ARX_ESTATE, "leave stress mode before changing its source");
-  if (pool == nullptr || sets == 0) {
-    S.stress_pool = nullptr;
-    S.stress_sets = 0;
-    return ARX_OK;
-  }
-  if (sets < 0) return fail(ARX_EINVAL, "sets %d < 0", sets);
-  if (!S.stress_stream) HIPCHK(hipStreamCreateWithFlags(&S.stress_stream, hipStreamNonBlocking));
-  S.stress_pool = (const uint16_t*)pool;
-  S.stress_sets = sets;
+  const bool clear = pool == nullptr || sets == 0;
+  if (!clear && sets < 0) return fail(ARX_EINVAL, "sets %d < 0", sets);
+  if (!clear && !S.stress_stream) HIPCHK(hipStreamCreateWithFlags(&S.stress_stream, hipStreamNonBlocking));
+  // under the proxy's lock: a stress post that read the mode before it
+  // left stress mode has finished with the old source
+  S.core->locked([&] {
+    S.stress_pool = clear ? nullptr : (const uint16_t*)pool;
+    S.stress_sets = clear ? 0 : sets;
+  });
   return ARX_OK;
 }
 

@@ -212,6 +212,64 @@ static void scenario_stress() {
   printf("ok %s\n", name);
 }
 
+// Leaving stress mode, then swapping the data source under locked(): once
+// locked() has returned, no data copy may run on the old source, nor start
+// at all, since the mode has left stress mode. Each round publishes new
+// seqs while holding the proxy's lock and waits, so the proxy has read the
+// new target (and the mode, still stress) and blocks on the lock; the mode
+// then leaves stress mode and the source is retired before the lock is
+// released. A proxy that copied data on the mode it read before taking the
+// lock would run the copy on the retired source.
+static void scenario_stress_switch() {
+  const char* name = "stress_switch";
+  struct Source {
+    bool valid;
+  };
+  Source good{true}, retired{false};
+  const Source* source = &good;  // read by before_post, replaced under locked()
+  int bad = 0;                   // written by before_post, under the lock
+  Words w;
+  arx::Proxy p(&w.pub, &w.done, w.flags, 4, 0);
+  p.before_post = [&](uint64_t) {
+    if (!source->valid) ++bad;
+    return true;
+  };
+  std::atomic<bool> stop{false};
+  std::thread t([&] { p.run(stop); });
+  uint64_t s = 0;
+  bool ok = true;
+  auto wait_flags = [&](uint64_t target) {
+    const auto t0 = std::chrono::steady_clock::now();
+    while (ld(&w.flags[1]) < target)
+      if (std::chrono::steady_clock::now() - t0 > 5s) return false;
+    return true;
+  };
+  for (int round = 0; round < 100 && ok; ++round) {
+    p.locked([&] { good.valid = true; source = &good; });
+    p.mode = arx::PROXY_STRESS;
+    s += 2;
+    st(&w.pub, s);  // two posts in stress mode, with their copies
+    ok = wait_flags(s);
+    p.locked([&] {
+      s += 2;
+      st(&w.pub, s);
+      std::this_thread::sleep_for(std::chrono::microseconds(300));
+      p.mode = arx::PROXY_LOCKSTEP;
+      good.valid = false;
+      source = &retired;
+    });
+    ok = ok && wait_flags(s);
+    st(&w.done, s);
+  }
+  stop = true;
+  t.join();
+  CHECK(ok, name, "the proxy stopped posting");
+  int nbad = 0;
+  p.locked([&] { nbad = bad; });
+  CHECK(nbad == 0, name, "%d data copies ran on a retired source", nbad);
+  printf("ok %s\n", name);
+}
+
 int main() {
   scenario_mode("lockstep", arx::PROXY_LOCKSTEP, 0);
   scenario_mode("runahead", arx::PROXY_RUNAHEAD, 1);
@@ -220,5 +278,6 @@ int main() {
   scenario_watchdog();
   scenario_concurrent_publish();
   scenario_stress();
+  scenario_stress_switch();
   return failures ? 1 : 0;
 }

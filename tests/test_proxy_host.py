@@ -22,7 +22,8 @@ def build(name, flags):
     return exe
 
 
-SCENARIOS = ["lockstep", "runahead", "manual", "no_skip_no_lead", "watchdog", "concurrent_publish", "stress"]
+SCENARIOS = ["lockstep", "runahead", "manual", "no_skip_no_lead", "watchdog", "concurrent_publish", "stress",
+             "stress_switch"]
 
 
 @pytest.mark.parametrize("variant,flags", [("plain", ["-O2"]), ("tsan", ["-O1", "-g", "-fsanitize=thread"])])
