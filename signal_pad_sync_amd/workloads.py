@@ -16,6 +16,10 @@ Workloads (bf16 elements n, W partials):
 
 Seeds: recv partial (par, src) of workload c uses 1000*c + 100*par + src; the
 own partial of call k uses 1000*c + 500 + k (k = 1, 2, ...).
+
+``bits`` draws raw bf16 patterns, every one of the 65536 equally likely
+(so about 1 in 256 is an Inf or a NaN): the limit tests use it for inputs
+at the largest size, where every pattern class should appear.
 """
 from typing import Dict, List
 
@@ -48,6 +52,11 @@ def normal(seed: int, n: int, scale: float = 1.0) -> np.ndarray:
 def uniform(seed: int, n: int, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return f32_to_bf16_trunc(rng.uniform(lo, hi, n))
+
+
+def bits(seed: int, n: int) -> np.ndarray:
+    """n uniformly random bf16 bit patterns."""
+    return np.random.default_rng(seed).integers(0, 1 << 16, size=n, dtype=np.uint16)
 
 
 def adversarial(seed: int, W: int, n: int) -> List[np.ndarray]:
