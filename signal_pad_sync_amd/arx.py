@@ -62,6 +62,13 @@ class ArxError(RuntimeError):
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"libarx.so not found at {path}; build it with signal_pad_sync_amd/build.py")
+    # One HIP runtime per process: torch's. The library receives torch's
+    # device pointers and streams, which only that runtime knows. Loaded
+    # first, libarx.so would bring in the system's runtime, and torch would
+    # then load its own copy beside it (torch's libraries name the runtime
+    # by another file name), and one of the two would see no device. torch
+    # loaded first, libarx.so binds to its runtime by soname.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     for name, res, args in SIGNATURES:
         f = getattr(L, name)
@@ -98,6 +105,25 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _buf(t, n: int, what: str, itemsize: int = 2):
+    """Device address of tensor t, after checking that it is a contiguous GPU
+    tensor of itemsize-byte elements holding at least n of them (the library
+    sees only the address, so it cannot check the extent itself)."""
+    if t is None:
+        if n > 0:
+            raise ArxError(EINVAL, f"{what} is None")
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ArxError(EINVAL, f"{what} must be a GPU tensor")
+    if t.element_size() != itemsize:
+        raise ArxError(EINVAL, f"{what} must have {itemsize}-byte elements, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ArxError(EINVAL, f"{what} must be contiguous")
+    if t.numel() < n:
+        raise ArxError(EINVAL, f"{what} holds {t.numel()} elements, fewer than {n}")
+    return t.data_ptr()
+
+
 def init(world: int, max_n: int, rank: int = 0):
     _check(lib.arx_init_rank(world, max_n, rank))
 
@@ -114,13 +140,13 @@ def allreduce(inp, out, n: int = None, stream=None):
     """One one-shot call: out[:n] = rank-ordered sum; inp/out bf16 tensors."""
     if n is None:
         n = inp.numel()
-    _check(lib.arx_allreduce(_ptr(inp), _ptr(out), n, _stream(stream)))
+    _check(lib.arx_allreduce(_buf(inp, n, "inp"), _buf(out, n, "out"), n, _stream(stream)))
 
 
 def reduce(inp, out, par: int, n: int = None, stream=None):
     if n is None:
         n = inp.numel()
-    _check(lib.arx_reduce(_ptr(inp), _ptr(out), n, par, _stream(stream)))
+    _check(lib.arx_reduce(_buf(inp, n, "inp"), _buf(out, n, "out"), n, par, _stream(stream)))
 
 
 def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, stream=None):
@@ -129,13 +155,18 @@ def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, str
 
 def counter_barrier(nblocks: int, rounds: int = 1, seen=None, stream=None):
     """seen: optional int32 device tensor [nblocks] receiving each block's epoch."""
-    _check(lib.arx_counter_barrier(nblocks, rounds, _ptr(seen), _stream(stream)))
+    ptr = None if seen is None else _buf(seen, nblocks, "seen", 4)
+    _check(lib.arx_counter_barrier(nblocks, rounds, ptr, _stream(stream)))
 
 
 def symm_allreduce(inputs, outputs, n: int, iters: int, stream=None):
     """inputs / outputs: bf16 device tensors [iters, W, ld] (ld >= n, ld % 8 == 0)."""
     ld = inputs.shape[-1]
-    _check(lib.arx_symm_allreduce(_ptr(inputs), _ptr(outputs), n, ld, iters, _stream(stream)))
+    if tuple(outputs.shape[-1:]) != (ld,):
+        raise ArxError(EINVAL, "inputs and outputs must have the same last dimension")
+    need = iters * world() * ld
+    _check(lib.arx_symm_allreduce(_buf(inputs, need, "inputs"), _buf(outputs, need, "outputs"), n, ld, iters,
+                                  _stream(stream)))
 
 
 def sem_view(rank: int):
@@ -154,8 +185,10 @@ def set_proxy_mode(mode: int):
 
 
 def set_stress_source(pool, sets: int):
-    """pool: bf16 device tensor [sets, W, max_n] (kept alive by the caller)."""
-    _check(lib.arx_set_stress_source(_ptr(pool), sets))
+    """pool: bf16 device tensor [sets, W, max_n] (kept alive by the caller);
+    None (or sets 0) clears the source."""
+    ptr = None if pool is None or sets == 0 else _buf(pool, max(sets, 0) * world() * max_n(), "pool")
+    _check(lib.arx_set_stress_source(ptr, sets))
 
 
 def set_timeout_us(us: int):
@@ -189,7 +222,9 @@ def world() -> int:
 
 
 def test_round_bf16(inp_u32, out_u16, stream=None):
-    _check(lib.arx_test_round_bf16(_ptr(inp_u32), _ptr(out_u16), inp_u32.numel(), _stream(stream)))
+    n = inp_u32.numel()
+    _check(lib.arx_test_round_bf16(_buf(inp_u32, n, "inp_u32", 4), _buf(out_u16, n, "out_u16"), n,
+                                   _stream(stream)))
 
 
 class _DevArray:
@@ -208,15 +243,24 @@ def _view(ptr, n, typestr, dtype):
     return t.view(dtype) if dtype is not None else t
 
 
+def _slot_len(n):
+    m = max_n()
+    if n is None:
+        return m
+    if not 0 < n <= m:
+        raise ArxError(EINVAL, f"a slot view holds 1 to max_n = {m} elements, not {n}")
+    return n
+
+
 def recv_view(par: int, src: int, n: int = None):
     """bf16 tensor viewing recv slot [par][src] (library memory, no copy)."""
     import torch
-    return _view(lib.arx_recv_ptr(par, src), n or max_n(), "<i2", torch.bfloat16)
+    return _view(lib.arx_recv_ptr(par, src), _slot_len(n), "<i2", torch.bfloat16)
 
 
 def send_view(par: int, n: int = None):
     import torch
-    return _view(lib.arx_send_ptr(par), n or max_n(), "<i2", torch.bfloat16)
+    return _view(lib.arx_send_ptr(par), _slot_len(n), "<i2", torch.bfloat16)
 
 
 def pad_view(rank: int):

@@ -300,6 +300,30 @@ def test_argument_errors():
         assert e.value.code == arx.ESTATE
 
 
+def test_binding_checks_tensor_extents():
+    """The binding passes only addresses to the library, so it checks that
+    every tensor is a contiguous GPU tensor of the right element size that
+    holds the elements the call touches, before anything is launched."""
+    with library(2, 1024):
+        t = torch.zeros(2048, dtype=torch.bfloat16, device="cuda")
+        short = torch.zeros(100, dtype=torch.bfloat16, device="cuda")
+        f32 = torch.zeros(2048, dtype=torch.float32, device="cuda")
+        host = torch.zeros(2048, dtype=torch.bfloat16)
+        symm_in = torch.zeros(2, 2, 512, dtype=torch.bfloat16, device="cuda")
+        for call in (lambda: arx.allreduce(t, short, 200), lambda: arx.allreduce(short, t, 101),
+                     lambda: arx.allreduce(f32, t, 8), lambda: arx.allreduce(host, t, 8),
+                     lambda: arx.allreduce(t[::2], t, 8), lambda: arx.reduce(t, short, 0, 200),
+                     lambda: arx.counter_barrier(8, 1, torch.zeros(4, dtype=torch.int32, device="cuda")),
+                     lambda: arx.symm_allreduce(symm_in, symm_in, 512, 3),
+                     lambda: arx.recv_view(0, 1, 1025), lambda: arx.send_view(1, 0)):
+            with pytest.raises(arx.ArxError) as e:
+                call()
+            assert e.value.code == arx.EINVAL
+        torch.cuda.synchronize()
+        d = arx.debug_state()
+        assert d["seq_dev"] == 0 and d["ctl_err"] == 0, d        # nothing was launched
+
+
 @pytest.mark.parametrize("W", [2, 4, 8])
 def test_barrier_leaves_pads_zero(W):
     """Page "triton_barrier.py": the pad is zero-filled again after every

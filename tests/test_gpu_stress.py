@@ -56,10 +56,13 @@ def test_stress_source_rules():
             arx.set_proxy_mode(arx.PROXY_STRESS)       # no source yet
         assert e.value.code == arx.EINVAL
         pool = torch.zeros(2 * 2 * 64, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(arx.ArxError) as e:
+            arx.set_stress_source(pool, 3)             # 3 sets do not fit in the pool
+        assert e.value.code == arx.EINVAL
         arx.set_stress_source(pool, 2)
         arx.set_proxy_mode(arx.PROXY_STRESS)
         with pytest.raises(arx.ArxError) as e:
-            arx.set_stress_source(pool, 3)             # not while in use
+            arx.set_stress_source(pool, 1)             # not while in use
         assert e.value.code == arx.ESTATE
         arx.set_proxy_mode(arx.PROXY_LOCKSTEP)
         arx.set_stress_source(None, 0)
