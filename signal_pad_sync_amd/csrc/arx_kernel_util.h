@@ -10,12 +10,14 @@
 
 namespace arx {
 
-// ---- buffer loads with an explicit cache policy ---------------------------
+// ---- buffer loads and stores with an explicit cache policy ---------------
 
 // Cache-policy bits of a gfx950 buffer instruction: sc0 = 1, nt = 2, sc1 = 16.
 enum : int {
   CP_SYS = 1 | 16,  // sc0 sc1: coherent at system scope, no stale cached copy
   CP_NT = 2,        // nontemporal: streamed, not kept in the caches
+  CP_DEV = 16,      // sc1: coherent at device scope; a store writes through
+                    // the L2 instead of staying dirty there
 };
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer, stride 0; loads
@@ -32,6 +34,11 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte
 template <int CP>
 __device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, CP);
+}
+
+template <int CP>
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CP);
 }
 
 __device__ __forceinline__ uint32_t slot_bytes(uint64_t stride) {

@@ -245,8 +245,10 @@ hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, int cus, hipSt
 // Workgroup b covers vectors [b * kBlock * U, (b + 1) * kBlock * U); thread t
 // handles vectors base + u * kBlock, u < U, issuing all U * W loads before
 // the first add. Inputs were written before the launch, so the loads are
-// nontemporal (stream through, keep nothing); the stores are plain, which
-// measured faster than nontemporal stores for this 8:1 read/write mix.
+// nontemporal (stream through, keep nothing). The stores write through the
+// L2 at device scope rather than staying dirty there; for this 8:1
+// read/write mix that measured 1.2 % faster than plain stores, while
+// nontemporal stores were 5 % slower.
 template <int W, int U>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
   const uint32_t nv = a.n >> 3, tail = a.n & 7u;
@@ -256,6 +258,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
   for (int src = 0; src < W; ++src)
     rs[src] = (src == a.rank) ? make_rsrc(a.in, a.n * 2u)
                               : make_rsrc(a.recv_par + (size_t)src * a.stride, slot_bytes(a.stride));
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.out, a.n * 2u);
   u32x4 x[U][W];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(ReduceArgs a) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t v = base + u * kBlock;
-    if (v < nv) st16(a.out + 8u * (size_t)v, sum_bf16x8<W>(x[u]));
+    if (v < nv) bstore16<CP_DEV>(ro, v * 16u, sum_bf16x8<W>(x[u]));
   }
   if (blockIdx.x == 0 && threadIdx.x < tail) {
     const uint32_t i = 8u * nv + threadIdx.x;
