@@ -29,20 +29,28 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "one-shot reduce GB/s (% of HBM peak) + µs/call at W=8, 256 KB bf16"
 
 
-def recorded_traffic(key):
+KERNEL_SOURCES = ("arx_reduce.hip", "arx_kernel_util.h", "arx_device.h", "arx_internal.h")
+
+
+def kernel_source_hash(csrc=os.path.join(ROOT, "signal_pad_sync_amd", "csrc")):
+    """sha256 over the sources of the reduction kernels, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(key, path=os.path.join(ROOT, "profiles", "hbm_traffic.json"), csrc=None):
     """HBM bytes per launch measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE
     runs summarised in profiles/hbm_traffic_pmc.md, or None when the kernel
     sources have changed since those counters were taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in ("arx_reduce.hip", "arx_kernel_util.h", "arx_device.h", "arx_internal.h"):
-        with open(os.path.join(ROOT, "signal_pad_sync_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return rec.get(key) if rec.get("kernel_source_sha256") == h.hexdigest() else None
+    current = kernel_source_hash(csrc) if csrc else kernel_source_hash()
+    return rec.get(key) if rec.get("kernel_source_sha256") == current else None
 
 
 def log(msg):
@@ -339,6 +347,35 @@ def cpu_baseline(seconds):
     return calls, dt
 
 
+def make_line(args, us_call, cpu, extra):
+    """The one JSON line: the headline workload's throughput, its roofline
+    and the CPU oracle's rate."""
+    W, n = 8, 131072
+    bytes_call = (W + 3) * 2 * n
+    value = bytes_call / us_call / 1e3 if us_call else None
+    # launches run back to back, so the event time of the timed region over
+    # the number of launches is the kernel's average launch duration
+    achieved = value
+    return {
+        "metric": METRIC, "value": round(value, 2) if value else None, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_call / 1e3, 6) if us_call else None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "one-shot reduce, W=8, bf16 [32,4096] per partial (n=131072), consecutive calls, "
+                               "parity alternating, lockstep host-proxy flags in pinned memory",
+                   "W": W, "n": n, "io_dtype": "bf16", "accumulate": "f32"},
+        "us_per_call": round(us_call, 3) if us_call else None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
+                     "traffic": recorded_traffic("oneshot_kernel_w8_n131072_bytes"),
+                     "kernel": "oneshot_kernel<8,true,256>", "bytes_per_launch": bytes_call,
+                     "kernel_us": round(us_call, 3) if us_call else None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -413,28 +450,7 @@ def main():
                "us_per_call": round(dt / calls * 1e6, 1)}
         log(f"  {cpu['us_per_call']} us/call on 1 core")
 
-    value = bytes_call / us_call / 1e3 if us_call else None
-    # launches run back to back, so the event time of the timed region over
-    # the number of launches is the kernel's average launch duration
-    achieved = value
-    line = {
-        "metric": METRIC, "value": round(value, 2) if value else None, "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(us_call / 1e3, 6) if us_call else None,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "one-shot reduce, W=8, bf16 [32,4096] per partial (n=131072), consecutive calls, "
-                               "parity alternating, lockstep host-proxy flags in pinned memory",
-                   "W": W, "n": n, "io_dtype": "bf16", "accumulate": "f32"},
-        "us_per_call": round(us_call, 3) if us_call else None,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
-                     "traffic": recorded_traffic("oneshot_kernel_w8_n131072_bytes"),
-                     "kernel": "oneshot_kernel<8,true,256>", "bytes_per_launch": bytes_call,
-                     "kernel_us": round(us_call, 3) if us_call else None},
-        "cpu_baseline": cpu,
-        "extra": extra,
-    }
+    line = make_line(args, us_call, cpu, extra)
     print(json.dumps(line), flush=True)
 
 
