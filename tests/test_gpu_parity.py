@@ -206,6 +206,17 @@ def test_sizes_tails_and_rank(W, rank):
         check_state(st, rank)
 
 
+def test_reduce_only_empty():
+    """The reduction alone at n = 0 launches nothing and writes nothing."""
+    with library(3, 1024):
+        inp, out = to_dev(np.ones(16, np.uint16)), sentinel(16)
+        note("reduce n=0")
+        arx.reduce(inp, out, 1, 0)
+        torch.cuda.synchronize()
+        assert np.all(to_host(out) == 0xDEAD)
+        assert arx.debug_state()["seq_dev"] == 0
+
+
 def test_grid_stride_path():
     """n beyond one vector per thread of the largest co-resident grid
     (256 workgroups x 1024 threads x 8 elements = 2 Mi), so each thread

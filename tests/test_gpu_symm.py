@@ -52,6 +52,22 @@ def test_symm_allreduce(W, n, iters):
             assert arx.debug_state()["ctl_err"] == 0
 
 
+def test_symm_empty():
+    """n = 0: the kernel still runs its barrier patterns (pads zero after),
+    writes nothing and raises no error."""
+    W, iters, ld = 4, 3, 8
+    with library(W, 64):
+        din = to_dev(np.ones(iters * W * ld, np.uint16)).view(iters, W, ld)
+        dout = to_dev(np.full(iters * W * ld, 0xDEAD, np.uint16)).view(iters, W, ld)
+        note("symm n=0")
+        arx.symm_allreduce(din, dout, 0, iters)
+        torch.cuda.synchronize()
+        assert np.all(to_host(dout) == 0xDEAD)
+        for r in range(W):
+            assert int(arx.pad_view(r).abs().sum()) == 0
+        assert arx.debug_state()["ctl_err"] == 0
+
+
 def test_symm_argument_errors():
     with library(2, 1024):
         t = torch.zeros(2 * 2 * 1024, dtype=torch.bfloat16, device="cuda").view(2, 2, 1024)
