@@ -119,6 +119,9 @@ int arx_publish(uint64_t seq);
  * earlier), ARX_ETIMEOUT (an earlier call's wait timed out), ARX_EHIP.
  * If this call's own flag wait times out on the device, out is left
  * untouched, seq still advances and the error is latched for the next call.
+ * The kernel's workgroups wait on each other, so its grid never exceeds
+ * what the device holds at once (occupancy per CU times the CU count, at
+ * most 256 workgroups); past one vector per thread, threads loop.
  */
 int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream);
 
@@ -166,7 +169,8 @@ int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t str
  * arx_symm_allreduce — an all-reduce among the W virtual ranks of this GPU
  * through symmetric buffers, fenced by the blockwise barrier's usage
  * patterns (page "triton_barrier.py", blockwise_barrier docstring): one
- * kernel of W * G workgroups (G per rank, all resident); at its start
+ * kernel of W * G workgroups (G per rank: about two 16-byte vectors per
+ * thread, at most 64, and all W * G resident at once); at its start
  * pattern 0; then for each of `iters` iterations every rank writes its
  * partial into its own symmetric buffer, passes pattern 1 (acq_rel, which
  * publishes the write to the matching blocks), reads its slice of every
@@ -217,6 +221,9 @@ int arx_set_proxy_mode(int mode);
  * stream of its own, waits for the copies, then posts the flags.
  *   pool: device bf16 [sets][W][max_n], owned by the caller, kept alive and
  *   unchanged while the mode is in use; sets >= 1. NULL / 0 clears it.
+ * Refused (ARX_ESTATE) while the stress mode is on; once the mode has been
+ * left, the call waits for a copy still in progress, and no copy reads the
+ * old source afterwards.
  * Errors: ARX_ESTATE, ARX_EINVAL, ARX_EHIP. A copy failure during the mode
  * latches ARX_EPROXY.
  */
