@@ -155,6 +155,7 @@ MUTANTS = {
     "M3": "proxy writes the flag before the data",
     "M4": "one counter shared by the arrival and the finish phase",
     "M5": "workgroups other than 0 do not wait for go",
+    "M6": "the arrival count publishes one copying workgroup early",
 }
 
 
@@ -171,8 +172,19 @@ class CheckResult:
 
 
 def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
-                   max_states: int = 5_000_000) -> CheckResult:
+                   max_states: int = 5_000_000, copiers: Optional[int] = None) -> CheckResult:
     """Explores every interleaving of W ranks x G workgroups x S calls.
+
+    copiers: the number C of workgroups that copy and count arrival (default
+    G, as on the page). Workgroup c < C copies every slice g with g % C == c
+    (a thread loop over a stride of C workgroups' vectors); the others skip
+    the copy and the arrival, and wait for go. The publish comes with the
+    C-th arrival. A workgroup reduces its own rank's partial from the
+    caller's input, which holds this call's data throughout the call; the
+    send slot is what the peers receive, through the proxy after the
+    publish. (With C < G a workgroup's own slice of the send slot may be
+    copied after its reduction: go follows the peers' flags, which do not
+    wait for this rank's copies.)
 
     Rank state tuple: (c, pcs, ss, cnt0, cnt1, go, seq_dev, ctl_seq, done,
     send, recv, flag, posted, pcur, ppos) where c is the running call (S + 1
@@ -183,6 +195,12 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
     """
     if mutant not in MUTANTS:
         raise ValueError(mutant)
+    C = G if copiers is None else copiers
+    if not 1 <= C <= G:
+        raise ValueError(f"copiers {C} not in [1, {G}]")
+    if mutant == "M6" and C < 2:
+        raise ValueError("M6 needs at least two copying workgroups")
+    last_arrival = C - 2 if mutant == "M6" else C - 1
     nbuf = 1 if mutant == "M2" else 2
 
     def par_of(s):
@@ -227,18 +245,21 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                     ns = None
                     if pc == READSEQ:
                         s2 = seq_dev + 1
-                        ns = (c, pcs[:g] + (COPY,) + pcs[g + 1:], ss[:g] + (s2,) + ss[g + 1:],
+                        nxt = COPY if g < C else WAIT
+                        ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss[:g] + (s2,) + ss[g + 1:],
                               cnt0, cnt1, go, seq_dev, ctl_seq, done, send, recv, flag, posted, pcur, ppos)
                     elif pc == COPY:
-                        i = par_of(s) * G + g
-                        send2 = send[:i] + (_tag(r, s),) + send[i + 1:]
+                        send2 = list(send)
+                        for g2 in range(g, G, C):
+                            send2[par_of(s) * G + g2] = _tag(r, s)
+                        send2 = tuple(send2)
                         ns = (c, pcs[:g] + (ARRIVE,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
                               ctl_seq, done, send2, recv, flag, posted, pcur, ppos)
                     elif pc == ARRIVE:
                         old = cnt0
                         n0 = cnt0 + 1
                         cs = ctl_seq
-                        if old == G - 1:      # last block publishes and resets
+                        if old == last_arrival:   # last copier publishes and resets
                             n0 = 0
                             cs = s
                         if mutant == "M4":    # one counter for both phases
@@ -258,7 +279,9 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                     elif pc == REDUCE:
                         p = par_of(s)
                         for j in range(W):
-                            t = send[p * G + g] if j == r else recv[(p * W + j) * G + g]
+                            if j == r:
+                                continue          # own partial: the caller's input
+                            t = recv[(p * W + j) * G + g]
                             if t != _tag(j, s):
                                 return CheckResult(False, len(seen), (
                                     f"rank {r} wg {g} reduced seq {s} with stale data from rank {j} "

@@ -41,6 +41,26 @@ def test_mutant_kinds():
     assert "stale" in P.check_protocol(2, 2, 3, mutant="M5").violation   # no go wait
 
 
+@pytest.mark.parametrize("W,G,S,C", [(2, 2, 3, 1), (2, 3, 2, 1), (2, 3, 2, 2), (3, 2, 2, 1), (2, 4, 2, 2)])
+def test_protocol_with_fewer_copying_workgroups(W, G, S, C):
+    """The kernel's variant: only the first C of G workgroups copy (each a
+    stride of C workgroups' slices) and count arrival; the publish comes
+    with the C-th arrival and every workgroup still waits for go."""
+    r = P.check_protocol(W, G, S, copiers=C)
+    assert r.ok, r.violation
+    assert r.finals == 1
+
+
+def test_publish_before_the_last_copier_is_caught():
+    """M6: publishing at the (C-1)-th arrival lets the proxy send a slice
+    the last copier has not written; caught with C = G and with C < G."""
+    for W, G, S, C in [(2, 2, 3, 2), (2, 3, 2, 2), (2, 4, 2, 2)]:
+        r = P.check_protocol(W, G, S, mutant="M6", copiers=C)
+        assert not r.ok and "stale" in r.violation, (W, G, S, C)
+    with pytest.raises(ValueError):
+        P.check_protocol(2, 2, 2, copiers=3)
+
+
 @pytest.mark.parametrize("W,K", [(2, 1), (2, 3), (2, 4), (3, 2), (3, 3)])
 def test_barrier_safe_live_and_zero(W, K):
     r = P.check_barrier(W, K)
