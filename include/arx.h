@@ -111,8 +111,8 @@ int arx_publish(uint64_t seq);
  * arx_allreduce). Launches one kernel on `stream`, asynchronously; the call
  * is hipGraph-capturable (each replay is the next seq).
  *   in:  device bf16 [n], this rank's partial, 16-byte aligned.
- *   out: device bf16 [n], 16-byte aligned; may alias `in`. out[i >= n] is
- *        never written.
+ *   out: device bf16 [n], 16-byte aligned; either `in` itself (in place)
+ *        or a range that does not overlap it. out[i >= n] is never written.
  *   n:   0 <= n <= max_n, any value (n % 8 != 0 allowed); n == 0 still runs
  *        the protocol and advances seq.
  * Errors (nothing launched): ARX_ESTATE, ARX_EINVAL, ARX_EPROXY (proxy failed

@@ -62,6 +62,7 @@ struct OneShotArgs {
   uint32_t n;
   int rank;
   uint64_t timeout;        // wall-clock ticks per wait
+  uint32_t ncopy;          // workgroups that copy and count arrival (set by the launcher)
 };
 
 struct ReduceArgs {
@@ -124,5 +125,7 @@ hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStr
 // workgroup, at most max_grid (all its workgroups must be resident at once,
 // since they wait on each other).
 unsigned oneshot_grid(uint32_t n, int block, unsigned max_grid);
+// Workgroups of a one-shot grid that copy the partial and count arrival.
+unsigned oneshot_copiers(unsigned grid);
 
 }  // namespace arx

@@ -255,7 +255,7 @@ int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream) {
   int rc = check_ready();
   if (rc != ARX_OK) return rc;
   if ((rc = check_ptrs(in, out, n)) != ARX_OK) return rc;
-  arx::OneShotArgs a;
+  arx::OneShotArgs a{};
   a.in = (const uint16_t*)in;
   a.out = (uint16_t*)out;
   a.send = S.send;

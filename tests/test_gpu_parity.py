@@ -240,19 +240,28 @@ def test_grid_stride_path():
         check_state(st, rank)
 
 
-def test_in_place():
-    """in and out may be the same buffer."""
-    W, n = 4, 100003
+@pytest.mark.parametrize("mode", [arx.PROXY_LOCKSTEP, arx.PROXY_RUNAHEAD])
+@pytest.mark.parametrize("n", [100003, 131072, (1 << 20) + 7])
+def test_in_place(mode, n):
+    """in and out may be the same buffer, at grids with and without the
+    copy split, also in run-ahead mode (go may then come before this rank's
+    publish): every output is the oracle's, and the send slot of each call
+    holds that call's input, not its output."""
+    W, K = 4, 4
     recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
-    x = WL.own_partial(3, 7, n)
-    with library(W, n + 5):
+    xs = [WL.own_partial(3, 7 + k, n) for k in range(K)]
+    with library(W, n + 5, mode=mode):
         fill_recv(recv, 0)
-        buf = to_dev(x, pad_to=n + 5)
-        note("in-place allreduce")
-        arx.allreduce(buf, buf, n)
-        torch.cuda.synchronize()
-        _, outs = P.sequential_model([(x, n)], recv, W, max_n=n + 5)
-        assert_bits(to_host(buf)[:n], outs[0], "in place")
+        st = None
+        for k in range(K):
+            buf = to_dev(xs[k], pad_to=n + 5)
+            note(f"in-place allreduce n={n} mode={mode} call {k + 1}")
+            arx.allreduce(buf, buf, n)
+            torch.cuda.synchronize()
+            st, outs = P.sequential_model([(xs[k], n)], recv, W, max_n=n + 5, state=st,
+                                          mode=P.RUNAHEAD if mode == arx.PROXY_RUNAHEAD else P.LOCKSTEP)
+            assert_bits(to_host(buf)[:n], outs[0], f"in place, call {k + 1}")
+            assert_bits(to_host(arx.send_view((k + 1) & 1, n)), xs[k], f"send slot of call {k + 1}")
 
 
 def test_manual_publish_and_order():
