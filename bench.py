@@ -369,7 +369,7 @@ def make_line(args, us_call, cpu, extra):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
                      "traffic": recorded_traffic("oneshot_kernel_w8_n131072_bytes"),
-                     "kernel": "oneshot_kernel<8,true,256>", "bytes_per_launch": bytes_call,
+                     "kernel": "oneshot_kernel<8,true,512>", "bytes_per_launch": bytes_call,
                      "kernel_us": round(us_call, 3) if us_call else None},
         "cpu_baseline": cpu,
         "extra": extra,

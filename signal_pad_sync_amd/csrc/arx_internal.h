@@ -48,7 +48,6 @@ enum : int {
 
 constexpr int kBlock = 256;       // threads per workgroup of the reduction kernels
 constexpr int kMaxOneShotGrid = 256;  // co-resident workgroups of the one-shot kernel
-constexpr int kOneShotTargetGrid = 64;  // one-shot workgroups the block size aims for
 
 struct OneShotArgs {
   const uint16_t* in;

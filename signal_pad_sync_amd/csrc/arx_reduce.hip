@@ -233,15 +233,18 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   return hipGetLastError();
 }
 
-// Threads per one-shot workgroup: the smallest of 256, 512 and 1024 that
-// keeps the grid within kOneShotTargetGrid workgroups, else 1024. Fewer
-// workgroups means fewer arrival atomics and fewer go pollers; measured on
-// MI355X at W=8 the call is fastest near 64 workgroups at every n from 8 Ki
-// to 4 Mi elements.
+// Threads per one-shot workgroup: 256 while that keeps the grid within 32
+// workgroups, 512 while that keeps it within 64 (where half of them copy),
+// else 1024. Fewer workgroups mean fewer arrivals, go pollers and
+// last-block-out atomics, more threads per workgroup a longer copy and
+// reduction per workgroup. Measured on MI355X at W=8, lockstep, for n from
+// 16 Ki to 768 Ki elements; at n = 128 Ki, 512 threads (32 workgroups)
+// take 8.36-8.39 us per call, 256 threads (64 workgroups, 32 copying)
+// 8.63-8.67 us and 1024 threads 9.04-9.07 us.
 int oneshot_block(uint32_t n) {
   const uint32_t nv = n >> 3;
-  for (int b : {256, 512})
-    if (nv <= (uint32_t)(b * kOneShotTargetGrid)) return b;
+  if (nv <= 256u * 32u) return 256;
+  if (nv <= 512u * 64u) return 512;
   return 1024;
 }
 
