@@ -6,6 +6,9 @@ definition computed with rationals on structured and random patterns, and an
 exhaustive sweep of all 2^32 patterns against torch's CPU float32 -> bfloat16
 conversion (a library routine) on every non-NaN input.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -54,21 +57,31 @@ def test_round_matches_definition_random():
 
 
 @pytest.mark.slow
+def _check_round_chunk(start, chunk):
+    pats = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
+    got = R.round_bf16(pats)
+    exp_field = (pats >> 23) & 0xFF
+    is_nan = (exp_field == 0xFF) & ((pats & 0x7FFFFF) != 0)
+    if not np.all(got[is_nan] == 0x7FC0):
+        return f"a NaN in the chunk at {hex(start)} did not give 0x7FC0"
+    t = torch.from_numpy(pats.view(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ok = is_nan | (got == t)
+    if not ok.all():
+        i = int(np.flatnonzero(~ok)[0])
+        return f"{hex(int(pats[i]))}: oracle {hex(int(got[i]))} torch {hex(int(t[i]))}"
+    return None
+
+
 def test_round_exhaustive_against_torch():
     """All 2^32 binary32 patterns: non-NaN inputs agree with torch's CPU
-    float32 -> bfloat16 (round to nearest even); every NaN gives 0x7FC0."""
+    float32 -> bfloat16 (round to nearest even); every NaN gives 0x7FC0.
+    Chunks run on a few threads (numpy, the oracle's C and torch release
+    the interpreter lock)."""
     chunk = 1 << 24
-    for start in range(0, 1 << 32, chunk):
-        pats = np.arange(start, start + chunk, dtype=np.uint64).astype(np.uint32)
-        got = R.round_bf16(pats)
-        exp_field = (pats >> 23) & 0xFF
-        is_nan = (exp_field == 0xFF) & ((pats & 0x7FFFFF) != 0)
-        assert np.all(got[is_nan] == 0x7FC0), hex(start)
-        t = torch.from_numpy(pats.view(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-        ok = is_nan | (got == t)
-        if not ok.all():
-            i = int(np.flatnonzero(~ok)[0])
-            raise AssertionError(f"{hex(int(pats[i]))}: oracle {hex(int(got[i]))} torch {hex(int(t[i]))}")
+    workers = max(1, min(8, (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for err in pool.map(lambda st: _check_round_chunk(st, chunk), range(0, 1 << 32, chunk)):
+            assert err is None, err
 
 
 def test_widen_exhaustive_against_definition_and_torch():
