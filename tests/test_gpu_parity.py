@@ -182,7 +182,7 @@ def test_workload5_adversarial():
         assert got2[n] == 0xDEAD
 
 
-@pytest.mark.parametrize("W,rank", [(3, 1), (5, 4), (8, 3)])
+@pytest.mark.parametrize("W,rank", [(3, 1), (5, 4), (6, 5), (7, 0), (8, 3)])
 def test_sizes_tails_and_rank(W, rank):
     """Any n (tails of 1..7, partial workgroups, n = 0), this GPU at rank r,
     one call after another; includes n past one pass of the co-resident grid."""
