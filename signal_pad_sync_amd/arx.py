@@ -101,10 +101,6 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def _ptr(t):
-    return None if t is None else t.data_ptr()
-
-
 def _buf(t, n: int, what: str, itemsize: int = 2):
     """Device address of tensor t, after checking that it is a contiguous GPU
     tensor of itemsize-byte elements holding at least n of them (the library
