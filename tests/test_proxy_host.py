@@ -2,7 +2,8 @@
 
 The proxy class (page "arx.cu", proxy_loop: post every seq in order, report
 stalls after 2 s) is built with g++ against a fake device thread in ordinary
-memory, once plainly and once under ThreadSanitizer (host code only)."""
+memory, once plainly, once under ThreadSanitizer and once under
+AddressSanitizer with UndefinedBehaviorSanitizer (host code only)."""
 import os
 import subprocess
 
@@ -26,12 +27,16 @@ SCENARIOS = ["lockstep", "runahead", "manual", "no_skip_no_lead", "watchdog", "c
              "stress_switch"]
 
 
-@pytest.mark.parametrize("variant,flags", [("plain", ["-O2"]), ("tsan", ["-O1", "-g", "-fsanitize=thread"])])
+@pytest.mark.parametrize("variant,flags", [("plain", ["-O2"]), ("tsan", ["-O1", "-g", "-fsanitize=thread"]),
+                                           ("asan_ubsan", ["-O1", "-g", "-fsanitize=address,undefined",
+                                                           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"])])
 def test_proxy_scenarios(variant, flags):
     exe = build(f"proxy_{variant}", flags)
-    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 second_deadlock_stack=1")
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 second_deadlock_stack=1",
+               ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
     assert r.returncode == 0, r.stdout + r.stderr
     for s in SCENARIOS:
         assert f"ok {s}" in r.stdout, r.stdout
     assert "WARNING: ThreadSanitizer" not in r.stderr, r.stderr
+    assert "ERROR: AddressSanitizer" not in r.stderr and "runtime error:" not in r.stderr, r.stderr
