@@ -65,15 +65,27 @@ def parse():
     ap.add_argument("--reduce-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,graph,reduce,barrier,symm; "
+    ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,floor,graph,reduce,barrier,symm; "
                     "configs (every workload, oracle included) runs only when named")
     return ap.parse_args()
 
 
-def timed(fn, steps, stream):
+# A spin kernel this long (GPU clock cycles, tens of ms) holds the stream
+# while the host enqueues the timed launches, so the events time the GPU
+# running them back to back, not the host issuing them.
+GATE_CYCLES = 200_000_000
+
+
+def timed(fn, steps, stream, gate=False):
+    """Event time of `steps` calls of fn on `stream`, in microseconds. With
+    gate, a spin kernel ahead of the start event keeps the GPU busy while
+    the host enqueues the calls (for launches shorter than the host's
+    enqueue cost)."""
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    if gate:
+        torch.cuda._sleep(GATE_CYCLES)
     start.record(stream)
     for _ in range(steps):
         fn()
@@ -116,7 +128,7 @@ def bench_oneshot(args, mode, graph=False):
             fn, reps = (lambda: rcs.append(call(xp, op, n, sh))), args.steps
         for _ in range(max(1, args.warmup // per)):
             fn()
-        us = timed(fn, reps, stream)
+        us = timed(fn, reps, stream, gate=not graph)
         calls = reps * per
         if not graph:
             assert not any(rcs), f"arx_allreduce failed: {set(rcs)}"
@@ -126,6 +138,34 @@ def bench_oneshot(args, mode, graph=False):
         torch.cuda.synchronize()
         arx.finalize()
     return us / calls, calls
+
+
+def bench_launch_floor(args):
+    """The smallest kernel of the library back to back: the reduction alone
+    at W=8 on one vector (n = 8), K launches through the C entry point with
+    its arguments prepared once; returns microseconds per launch. It is what
+    one dependent launch costs on this stream, the reference for the
+    one-shot call's latency."""
+    import torch
+    from signal_pad_sync_amd import arx
+
+    W, n = 8, 8
+    arx.init(W, 1024)
+    try:
+        x = torch.zeros(n, device="cuda", dtype=torch.bfloat16)
+        out = torch.empty_like(x)
+        stream = torch.cuda.current_stream()
+        call, xp, op, sh = arx.lib.arx_reduce, x.data_ptr(), out.data_ptr(), stream.cuda_stream
+        rcs = []
+        fn = lambda: rcs.append(call(xp, op, n, 0, sh))
+        for _ in range(args.warmup):
+            fn()
+        us = timed(fn, args.steps, stream, gate=True) / args.steps
+        assert not any(rcs), f"arx_reduce failed: {set(rcs)}"
+    finally:
+        torch.cuda.synchronize()
+        arx.finalize()
+    return us
 
 
 def bench_reduce(args):
@@ -407,6 +447,10 @@ def main():
         us_ra, _ = bench_oneshot(args, arx.PROXY_RUNAHEAD)
         extra["runahead_us_per_call"] = round(us_ra, 3)
         log(f"  {us_ra:.2f} us/call")
+    if want("floor"):
+        log("launch floor: the reduction alone on one vector, back to back")
+        extra["launch_floor_us"] = round(bench_launch_floor(args), 3)
+        log(f"  {extra['launch_floor_us']:.2f} us/launch")
     if want("graph"):
         log("one-shot, lockstep proxy, 100 calls per hipGraph")
         us_g, _ = bench_oneshot(args, arx.PROXY_LOCKSTEP, graph=True)
