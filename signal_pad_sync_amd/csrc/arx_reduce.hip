@@ -233,8 +233,11 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   return hipGetLastError();
 }
 
-// Threads per one-shot workgroup: 256 while that keeps the grid within 32
-// workgroups, 512 while that keeps it within 64 (where half of them copy),
+// Threads per one-shot workgroup. Up to 1024 vectors: one workgroup of the
+// smallest size that holds them, so nothing waits on the go broadcast
+// (0.4-0.6 us faster than 2 or 4 workgroups at n = 4 Ki and 8 Ki for W
+// from 2 to 8; at W = 8, n = 8 Ki, a tie). Beyond: 256 while that keeps the
+// grid within 32 workgroups, 512 while within 64 (where half of them copy),
 // else 1024. Fewer workgroups mean fewer arrivals, go pollers and
 // last-block-out atomics, more threads per workgroup a longer copy and
 // reduction per workgroup. Measured on MI355X at W=8, lockstep, for n from
@@ -243,6 +246,9 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
 // 8.63-8.67 us and 1024 threads 9.04-9.07 us.
 int oneshot_block(uint32_t n) {
   const uint32_t nv = n >> 3;
+  if (nv <= 256u) return 256;
+  if (nv <= 512u) return 512;
+  if (nv <= 1024u) return 1024;
   if (nv <= 256u * 32u) return 256;
   if (nv <= 512u * 64u) return 512;
   return 1024;
