@@ -72,8 +72,13 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // 2. arrival count: one system-scope release per copying workgroup
   //    carries all its waves' copies (they precede it through the workgroup
   //    barrier); the last to arrive acquires them all, resets the counter
-  //    and publishes seq to the host proxy
-  if (copier && threadIdx.x == 0) {
+  //    and publishes seq to the host proxy. A grid of one workgroup is its
+  //    own last arrival: its release store of seq carries the copies.
+  const bool single = gridDim.x == 1u;
+  if (single && threadIdx.x == 0) {
+    store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
+    store_release_system(&a.ctl->seq, seq);
+  } else if (copier && threadIdx.x == 0) {
     if (fetch_add_release_system(cnt0, 1u) == a.ncopy - 1u) {
       fence_acquire_system();
       store_relaxed_agent(cnt0, 0u);
@@ -106,7 +111,8 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
         store_relaxed_agent(abort_w, seq);
         report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
       }
-      store_release_agent(go, seq32);
+      if (single) store_relaxed_agent(go, seq32);   // no other workgroup waits on it
+      else store_release_agent(go, seq32);
     }
     abort = bad != 0;
   } else {
@@ -162,12 +168,16 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
     }
   }
 
-  // 5. last block out: reset the finish counter, record the completed seq.
+  // 5. last block out: reset the finish counter, record the completed seq
+  //    (a grid of one workgroup is its own last block and needs no count).
   //    Relaxed: the only reader of the counter and of seq_dev is the next
   //    kernel on the stream, which the kernel boundary already orders after
   //    this one; ctl.done is progress information for the host.
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (single && threadIdx.x == 0) {
+    store_relaxed_agent(seq_dev, seq);
+    store_relaxed_system(&a.ctl->done, seq);
+  } else if (threadIdx.x == 0) {
     if (fetch_add_relaxed_agent(cnt1, 1u) == gridDim.x - 1u) {
       store_relaxed_agent(cnt1, 0u);
       store_relaxed_agent(seq_dev, seq);
