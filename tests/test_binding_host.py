@@ -82,3 +82,10 @@ def test_one_hip_runtime_per_process():
             "assert sum('libhsa-runtime64' in x for x in libs) == 1, libs\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """There is no fallback path: without libarx.so the binding refuses to
+    load."""
+    with pytest.raises(ImportError, match="libarx.so not found"):
+        arx.load(str(tmp_path / "libarx.so"))
