@@ -84,7 +84,7 @@ def timed(fn, steps, stream, gate=False):
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    if gate:
+    if gate and hasattr(torch.cuda, "_sleep"):   # without it the timing is merely ungated
         torch.cuda._sleep(GATE_CYCLES)
     start.record(stream)
     for _ in range(steps):
