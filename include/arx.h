@@ -77,6 +77,9 @@ extern "C" {
  * thread started). This GPU is rank 0.
  *   world: W in [2, 8].  max_n: largest n any later call may use, in bf16
  *   elements, 1 <= max_n <= ARX_MAX_N.
+ * The proxy thread busy-polls the published seq (one host core) from here
+ * until arx_finalize, as the page's proxy_loop does; its poll latency is
+ * part of every call's flag wait.
  * Allocates on the current HIP device: send slots [2][max_n], recv slots
  * [2][W][max_n] and symmetric buffers [W][max_n] bf16 in device memory, W
  * signal pads u32[ARX_MAX_PAD_BLOCKS][W], W x ARX_MAX_PAD_BLOCKS semaphores
