@@ -259,6 +259,14 @@ int arx_debug_state(uint64_t* words, int nwords);
  * flight. Errors: ARX_ESTATE, ARX_EHIP. */
 int arx_debug_set_seq(uint64_t seq);
 
+/* Test aid: the proxy's next post in ARX_PROXY_STRESS mode fails, as a
+ * failed copy of the peers' data would. The proxy thread then stops and the
+ * failure is latched: the next arx_allreduce (or any call that launches)
+ * returns ARX_EPROXY until arx_finalize, as the page's proxy error latch
+ * makes the next all-reduce throw. A call already in flight never gets its
+ * flags and ends through its bounded wait. Errors: ARX_ESTATE. */
+int arx_debug_fail_proxy(void);
+
 /* The binary32 -> bf16 rounding of the reduction alone (for exhaustive
  * checks): out[i] = the bf16 pattern the reduction writes for the binary32
  * pattern in[i]. in: device u32 [n], out: device u16 [n]; n <= 2^32 - 1. */

@@ -45,6 +45,7 @@ SIGNATURES = [
     ("arx_status", _c.c_int, [_u64p, _u64p, _u64p]),
     ("arx_debug_state", _c.c_int, [_u64p, _c.c_int]),
     ("arx_debug_set_seq", _c.c_int, [_c.c_uint64]),
+    ("arx_debug_fail_proxy", _c.c_int, []),
     ("arx_test_round_bf16", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     ("arx_strerror", _c.c_char_p, [_c.c_int]),
     ("arx_max_n", _c.c_size_t, []),
@@ -207,6 +208,10 @@ def debug_state() -> dict:
 
 def debug_set_seq(seq: int):
     _check(lib.arx_debug_set_seq(seq))
+
+
+def debug_fail_proxy():
+    _check(lib.arx_debug_fail_proxy())
 
 
 def max_n() -> int:

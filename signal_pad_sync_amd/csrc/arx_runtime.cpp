@@ -50,6 +50,7 @@ struct State {
   std::unique_ptr<arx::Proxy> core;  // flag posting and the stall watchdog
   std::thread proxy;
   std::atomic<bool> proxy_err{false};
+  std::atomic<bool> inject_copy_failure{false};  // test aid: the next stress copy fails
   std::atomic<bool> stop{false};
   const uint16_t* stress_pool = nullptr;  // device [sets][W][max_n], caller-owned
   int stress_sets = 0;
@@ -109,6 +110,7 @@ uint64_t timeout_ticks() { return S.timeout_us * S.clock_khz / 1000u; }
 
 // The peers' data for seq s, written before its flag (ARX_PROXY_STRESS).
 bool stress_copy(uint64_t s) {
+  if (S.inject_copy_failure.exchange(false)) return false;
   if (!S.stress_pool || !S.stress_stream) return false;
   const int par = (int)(s & 1);
   const uint16_t* set = S.stress_pool + (size_t)(s % (uint64_t)S.stress_sets) * S.world * S.max_n;
@@ -196,6 +198,7 @@ int init_impl(int world, size_t max_n, int rank) {
   memset((void*)S.ctl, 0, 4096);
   memset((void*)S.flags, 0, 4096);
   S.proxy_err.store(false);
+  S.inject_copy_failure.store(false);
   S.stop.store(false);
   S.timeout_us = 2000000;
   // no C++ exception may leave the C ABI
@@ -454,6 +457,12 @@ int arx_debug_set_seq(uint64_t seq) {
   store_release(&S.ctl->done, seq);
   store_release(&S.ctl->seq, seq);
   S.core->reset(seq);
+  return ARX_OK;
+}
+
+int arx_debug_fail_proxy(void) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  S.inject_copy_failure.store(true);
   return ARX_OK;
 }
 
