@@ -89,3 +89,26 @@ def test_proxy_failure_is_latched():
         assert e.value.code == arx.EPROXY
         d = arx.debug_state()
         assert d["seq_dev"] == 1 and d["posted"] == 0 and d["ctl_err"] != 0, d
+
+
+def test_watchdog_reports_a_dead_peer(capfd):
+    """Page "arx.cu", proxy_loop: a rank whose published work has not
+    finished for 2 s prints one STALL line with what it published, posted
+    and finished and each peer's flag. Forced from the host: manual mode
+    and no publish, so the call waits for flags that never come, bounded at
+    3 s; the report must appear while it waits."""
+    import time
+    W, n = 3, 1024
+    with library(W, n, mode=arx.PROXY_MANUAL, timeout_us=3_000_000):
+        inp, out = to_dev(WL.normal(8900, n)), to_dev(np.full(n, 0xDEAD, np.uint16))
+        note("watchdog: one call whose peers never publish, 3 s bound")
+        arx.allreduce(inp, out, n)
+        time.sleep(2.5)
+        published, posted, done = arx.status()
+        assert (published, posted, done) == (1, 0, 0), (published, posted, done)
+        torch.cuda.synchronize()                     # the 3 s flag wait ends the call
+        err = capfd.readouterr().err
+        assert "STALL: published 1 posted 0 done 0" in err, err
+        assert err.count("STALL") == 1, err
+        assert np.all(to_host(out) == 0xDEAD)
+        assert arx.debug_state()["ctl_err"] != 0
