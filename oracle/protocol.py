@@ -473,7 +473,7 @@ ADDING, WAITING, STAGE_DONE = range(3)
 
 
 def check_counter_barrier(W: int, K: int, mutant: Optional[str] = None, strong: str = "",
-                          max_states: int = 5_000_000) -> CheckResult:
+                          max_states: int = 5_000_000, split_stages: bool = False) -> CheckResult:
     """Explores every interleaving of W ranks running K rounds of (start
     stage, end stage) on one block id.
 
@@ -486,6 +486,11 @@ def check_counter_barrier(W: int, K: int, mutant: Optional[str] = None, strong: 
     but not for W >= 3, where a rank that is a stage ahead can add to r's
     flag in place of a slow rank's pending add.
 
+    split_stages: a repair, not the page's design. Every rank has two
+    semaphores per block, one that start stages add to and one for end
+    stages, each waited for up to W per stage; a rank a stage ahead then
+    cannot add to the flag a slow rank's pending add is due on.
+
     State: (stage_idx, added, waiting, flag, base). stage_idx[r] counts the
     stages rank r has entered (0-based; stage 2k is round k's start, 2k+1
     its end; 2K once finished); added[r] is the set (bitmask) of lanes of
@@ -496,7 +501,8 @@ def check_counter_barrier(W: int, K: int, mutant: Optional[str] = None, strong: 
     if mutant not in COUNTER_MUTANTS:
         raise ValueError(mutant)
     full = (1 << W) - 1
-    init = ((0,) * W, (0,) * W, (0,) * W, (0,) * W, (0,) * W)
+    nf = 2 if split_stages else 1           # semaphores per rank
+    init = ((0,) * W, (0,) * W, (0,) * W, (0,) * (nf * W), (0,) * (nf * W))
     seen = {init}
     stack = [init]
     finals = 0
@@ -509,19 +515,22 @@ def check_counter_barrier(W: int, K: int, mutant: Optional[str] = None, strong: 
             if si >= 2 * K:
                 continue
             start = si % 2 == 0
+            sem = (0 if start else 1) if split_stages else 0   # which of a rank's semaphores
             # a lane that has not added yet adds 1 to its rank's flag
             if not waiting[r]:
                 for w in range(W):
                     if not added[r] >> w & 1:
-                        flag2 = flag[:w] + (flag[w] + 1,) + flag[w + 1:]
+                        fw = w * nf + sem
+                        flag2 = flag[:fw] + (flag[fw] + 1,) + flag[fw + 1:]
                         added2 = added[:r] + (added[r] | (1 << w),) + added[r + 1:]
                         waiting2 = waiting
                         if added2[r] == full:
                             waiting2 = waiting[:r] + (1,) + waiting[r + 1:]
                         succ.append((stage_idx, added2, waiting2, flag2, base))
             else:
-                target = W * (1 if start else 2)
-                have = flag[r] - base[r]
+                fr = r * nf + sem
+                target = W if split_stages else W * (1 if start else 2)
+                have = flag[fr] - base[fr]
                 ok = have == target if mutant == "C2" else have >= target
                 if ok:
                     # rank r leaves this stage: every rank must have added for it
@@ -533,12 +542,15 @@ def check_counter_barrier(W: int, K: int, mutant: Optional[str] = None, strong: 
                         if not q_added:
                             return CheckResult(False, len(seen), (
                                 f"rank {r} left stage {si} before rank {q} arrived at it"))
-                    b = base[r]
-                    if not start and mutant != "C1":
-                        b = base[r] + 2 * W
-                    if start and mutant == "C3":
-                        b = base[r] + W
-                    base2 = base[:r] + (b,) + base[r + 1:]
+                    b = base[fr]
+                    if split_stages:
+                        b = base[fr] + W
+                    else:
+                        if not start and mutant != "C1":
+                            b = base[fr] + 2 * W
+                        if start and mutant == "C3":
+                            b = base[fr] + W
+                    base2 = base[:fr] + (b,) + base[fr + 1:]
                     stage2 = stage_idx[:r] + (si + 1,) + stage_idx[r + 1:]
                     added2 = added[:r] + (0,) + added[r + 1:]
                     waiting2 = waiting[:r] + (0,) + waiting[r + 1:]
@@ -547,8 +559,9 @@ def check_counter_barrier(W: int, K: int, mutant: Optional[str] = None, strong: 
             if not all(x == 2 * K for x in stage_idx):
                 return CheckResult(False, len(seen), (
                     f"deadlock: stages {stage_idx} flags {flag} bases {base}"))
-            if any(f != 2 * W * K for f in flag) or any(b != 2 * W * K for b in base):
-                return CheckResult(False, len(seen), f"final flags {flag} bases {base}, want {2 * W * K}")
+            want = W * K if split_stages else 2 * W * K
+            if any(f != want for f in flag) or any(b != want for b in base):
+                return CheckResult(False, len(seen), f"final flags {flag} bases {base}, want {want}")
             finals += 1
         for s2 in succ:
             if s2 not in seen:

@@ -149,6 +149,19 @@ def test_counter_barrier_per_flag_pairing():
     assert not r.ok and "left stage 1" in r.violation
 
 
+def test_counter_barrier_split_stages_restore_the_pairing():
+    """A repair, not the page's design: with one semaphore for start stages
+    and one for end stages, a rank a stage ahead cannot add to the flag a
+    slow rank's pending add is due on, and the per-flag pairing holds where
+    the single-semaphore design loses it (W = 3 over two rounds) and at
+    W = 4."""
+    for W, K in [(3, 2), (3, 3), (4, 2)]:
+        r = P.check_counter_barrier(W, K, strong="all", split_stages=True)
+        assert r.ok, (W, K, r.violation)
+        assert r.finals == 1
+    assert not P.check_counter_barrier(3, 2, strong="end").ok   # the page's design, for contrast
+
+
 def test_epochs_alternate():
     assert [P.epochs_after(k) for k in range(5)] == [0, 1, 0, 1, 0]
 
