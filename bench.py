@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "one-shot reduce GB/s (% of HBM peak) + µs/call at W=8, 256 KB bf16"
 
 
-KERNEL_SOURCES = ("arx_reduce.hip", "arx_kernel_util.h", "arx_device.h", "arx_internal.h")
+KERNEL_SOURCES = ("arx_reduce.hip", "arx_kernel_util.h", "arx_prims.h", "arx_internal.h")
 
 
 def kernel_source_hash(csrc=os.path.join(ROOT, "signal_pad_sync_amd", "csrc")):
@@ -202,12 +202,28 @@ def bench_reduce(args):
     return samples[len(samples) // 2], us_total / args.reduce_reps
 
 
-def bench_barrier(args, sem):
-    """256-workgroup barrier at W=8, 100 launches per hipGraph; returns
-    microseconds per launch. sem: a signal-pad semantics, or "counter" for
-    one round (start + end stage) of the counter barrier."""
+BARRIER_KINDS = {
+    # name: (counter barrier?, sem or flags)
+    "pad_acq_rel": (False, 1, 0),
+    "pad_relaxed": (False, 0, 0),
+    "pad_acq_rel_lanes": (False, 1, 1),
+    "pad_relaxed_lanes": (False, 0, 1),
+    "counter_page": (True, None, 0),
+    "counter_split": (True, None, 2),
+    "counter_page_lanes": (True, None, 1),
+}
+
+
+def bench_barrier(args, kind):
+    """One barrier round on 256 block ids at W=8, 100 launches per hipGraph;
+    returns microseconds per launch. Default launches give every virtual
+    rank's block a workgroup of its own (2048 workgroups that wait on each
+    other); the _lanes variants put the 8 ranks of a block in one wave (256
+    workgroups, none waiting on another). counter_*: one round (start + end
+    stage) of the counter barrier, page design or split stages."""
     import torch
     from signal_pad_sync_amd import arx
+    counter, sem, flags = BARRIER_KINDS[kind]
     arx.init(8, 1024)
     try:
         stream = torch.cuda.current_stream()
@@ -215,10 +231,10 @@ def bench_barrier(args, sem):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(per):
-                if sem == "counter":
-                    arx.counter_barrier(256, 1)
+                if counter:
+                    arx.counter_barrier(256, 1, flags)
                 else:
-                    arx.barrier_blockwise(256, sem, 1)
+                    arx.barrier_blockwise(256, sem, 1, flags)
         for _ in range(3):
             g.replay()
         reps = max(1, args.steps // per)
@@ -367,24 +383,45 @@ def bench_configs(args):
     return rows
 
 
-def cpu_baseline(seconds):
-    """The oracle's one-shot model (sequential protocol + C reduction) on the
-    headline workload, single-threaded, for about `seconds` of CPU time."""
+def cpu_baseline(seconds, threads=1):
+    """The oracle's one-shot model (sequential protocol + C reduction, the
+    reduction on `threads` host threads) on the headline workload, for
+    about `seconds` of wall time; returns (calls, seconds)."""
     from oracle import protocol as P
     from signal_pad_sync_amd import workloads as WL
 
     W, n = 8, 131072
     recv = [WL.recv_partials(2, par, n) for par in (0, 1)]
     x = WL.own_partial(2, 1, n)
-    st = None
     t0 = time.perf_counter()
-    st, _ = P.sequential_model([(x, n)] * 10, recv, W)
+    P.sequential_model([(x, n)] * 10, recv, W, threads=threads)
     per = (time.perf_counter() - t0) / 10
     calls = max(10, int(seconds / per))
     t0 = time.perf_counter()
-    st, _ = P.sequential_model([(x, n)] * calls, recv, W)
+    P.sequential_model([(x, n)] * calls, recv, W, threads=threads)
     dt = time.perf_counter() - t0
     return calls, dt
+
+
+def cpu_leg(seconds):
+    """cpu_baseline of the JSON line: the oracle on every host core this
+    process may use (T threads, stated), with the one-core figure beside it."""
+    W, n = 8, 131072
+    bytes_call = (W + 3) * 2 * n
+    T = len(os.sched_getaffinity(0))
+    out = None
+    for threads in (T, 1):
+        calls, dt = cpu_baseline(seconds / 2, threads)
+        leg = {"value": round(bytes_call * calls / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{calls} one-shot calls of the headline workload (W=8, n=131072): the sequential protocol "
+                         f"model with the C reduction on {threads} thread(s), contiguous index ranges",
+               "us_per_call": round(dt / calls * 1e6, 1)}
+        log(f"  {leg['us_per_call']} us/call on {threads} thread(s)")
+        if out is None:
+            out = leg
+        else:
+            out["one_core"] = leg
+    return out
 
 
 def make_line(args, us_call, cpu, extra):
@@ -410,7 +447,7 @@ def make_line(args, us_call, cpu, extra):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
                      "traffic": recorded_traffic("oneshot_kernel_w8_n131072_bytes"),
                      "kernel": "oneshot_kernel<8,true,512>", "bytes_per_launch": bytes_call,
-                     "kernel_us": round(us_call, 3) if us_call else None},
+                     "event_us_per_launch": round(us_call, 3) if us_call else None},
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -468,10 +505,10 @@ def main():
         log(f"  {mean:.1f} us per launch back to back ({med:.1f} us median timed one by one), "
             f"{rb / mean / 1e3:.0f} GB/s")
     if want("barrier"):
-        for name, sem in (("acq_rel", arx.SEM_ACQ_REL), ("relaxed", arx.SEM_RELAXED), ("counter", "counter")):
-            log(f"barrier ({name}), 256 workgroups, W=8, 100 launches per hipGraph")
-            us_b = bench_barrier(args, sem)
-            extra[f"barrier_256wg_{name}_us"] = round(us_b, 3)
+        for kind in BARRIER_KINDS:
+            log(f"barrier {kind}, 256 block ids, W=8, 100 launches per hipGraph")
+            us_b = bench_barrier(args, kind)
+            extra[f"barrier_w8_256blk_{kind}_us"] = round(us_b, 3)
             log(f"  {us_b:.3f} us/launch")
 
     if args.only and "configs" in only:
@@ -488,11 +525,7 @@ def main():
     cpu = None
     if not args.skip_cpu:
         log(f"oracle on the CPU, ~{args.cpu_seconds} s")
-        calls, dt = cpu_baseline(args.cpu_seconds)
-        cpu = {"value": round(bytes_call * calls / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{calls} one-shot calls (sequential protocol model + C reduction), W=8, n=131072",
-               "us_per_call": round(dt / calls * 1e6, 1)}
-        log(f"  {cpu['us_per_call']} us/call on 1 core")
+        cpu = cpu_leg(args.cpu_seconds)
 
     line = make_line(args, us_call, cpu, extra)
     print(json.dumps(line), flush=True)

@@ -70,6 +70,25 @@ extern "C" {
 #define ARX_SEM_RELAXED 0 /* relaxed system-scope CAS on both sides */
 #define ARX_SEM_ACQ_REL 1 /* release CAS to signal, acquire CAS to consume */
 
+/* Barrier launch flags. By default rank v's block b is a workgroup of its
+ * own: W * nblocks workgroups, the W with block id b wait on each other. */
+#define ARX_BARRIER_LANES 1 /* the named lane-group variant: workgroup b is one wave whose lanes
+                               [v*W, v*W + W) play rank v, so no workgroup waits on another */
+#define ARX_BARRIER_SPLIT 2 /* counter barrier only: separate start- and end-stage semaphores */
+
+/*
+ * Barrier tags. A tagged barrier launch checks what each round makes
+ * visible: before round r, rank v's workgroup for block b writes the tag
+ *     tag(v, b, r) = 0x80000000 | r << 16 | b << 4 | v
+ * with a plain store into tags[(v * rounds + r) * nblocks + b]; after the
+ * round its thread p < W reads rank p's tag for the same block and round
+ * with a plain load into seen[((v * rounds + r) * nblocks + b) * W + p].
+ * Every round has slots of its own. With ARX_SEM_ACQ_REL the barrier makes
+ * the peers' tags visible, so seen holds tag(p, b, r) everywhere; with
+ * ARX_SEM_RELAXED a slot may still read as its earlier contents. The caller
+ * zero-fills both buffers before the launch.
+ */
+
 /*
  * arx_init — allocate and zero all state, start the proxy thread.
  * Page "arx.cu": arx_prepare (world range check, pinned flag and control
@@ -83,7 +102,7 @@ extern "C" {
  * Allocates on the current HIP device: send slots [2][max_n], recv slots
  * [2][W][max_n] and symmetric buffers [W][max_n] bf16 in device memory, W
  * signal pads u32[ARX_MAX_PAD_BLOCKS][W], W x ARX_MAX_PAD_BLOCKS semaphores
- * and ARX_MAX_PAD_BLOCKS epochs,
+ * and W x ARX_MAX_PAD_BLOCKS epochs,
  * the device words (seq, two counters, go, abort), and in pinned coherent
  * host memory the control block and flags[W] (u64). Errors: ARX_EINVAL,
  * ARX_ESTATE (already initialised), ARX_ENOMEM, ARX_EHIP.
@@ -115,7 +134,8 @@ int arx_publish(uint64_t seq);
  * is hipGraph-capturable (each replay is the next seq).
  *   in:  device bf16 [n], this rank's partial, 16-byte aligned.
  *   out: device bf16 [n], 16-byte aligned; either `in` itself (in place)
- *        or a range that does not overlap it. out[i >= n] is never written.
+ *        or a range that does not overlap it (a partial overlap is
+ *        ARX_EINVAL). out[i >= n] is never written.
  *   n:   0 <= n <= max_n, any value (n % 8 != 0 allowed); n == 0 still runs
  *        the protocol and advances seq.
  * Errors (nothing launched): ARX_ESTATE, ARX_EINVAL, ARX_EPROXY (proxy failed
@@ -137,36 +157,64 @@ int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream);
 int arx_reduce(const void* in, void* out, size_t n, int par, hipStream_t stream);
 
 /*
- * arx_barrier_blockwise — launch `nblocks` workgroups; workgroup b runs the
- * blockwise signal-pad barrier on block id b for all W virtual ranks (page
- * "triton_barrier.py": blockwise_barrier, send_signal, wait_signal): in the
- * workgroup's single wave, lanes [v*W, v*W + W) play rank v, and its lane s
- * CASes slot v of block b in rank s's pad from 0 to 1 and then CASes slot s
- * of block b in its own pad from 1 to 0. The
+ * arx_barrier_blockwise — the blockwise signal-pad barrier (page
+ * "triton_barrier.py": blockwise_barrier, send_signal, wait_signal) for the
+ * W virtual ranks on block ids 0..nblocks-1, `rounds` consecutive times.
+ * Each rank's part on block b runs the device function barrier_blockwise of
+ * arx_device.h on the library's pads (lane s < W CASes slot (b, v) of rank
+ * s's pad from 0 to 1, then slot (b, s) of its own pad from 1 to 0). The
  * pads start zero-filled and are zero-filled again after every barrier, so
  * the launch is hipGraph-capturable with no host reset.
+ *   Default launch: W * nblocks workgroups of one wave; workgroup g plays
+ *   rank g % W's block g / W, so the W workgroups of a block id are
+ *   consecutive and run on different XCDs. They wait on each other, so
+ *   W * nblocks must not exceed what the device holds at once (the kernel's
+ *   occupancy per CU times the CU count), else ARX_EINVAL. With acq_rel each
+ *   round follows the page's usage pattern 1 (workgroup barrier, barrier,
+ *   workgroup barrier), with relaxed pattern 0.
+ *   flags & ARX_BARRIER_LANES: nblocks workgroups of one wave, lanes
+ *   [v*W, v*W + W) of workgroup b playing rank v; every signal precedes
+ *   every consume in one instruction stream and no workgroup waits on
+ *   another (it measures the atomics and fences alone).
  *   nblocks: 1..ARX_MAX_PAD_BLOCKS.  sem: ARX_SEM_RELAXED or ARX_SEM_ACQ_REL.
- *   rounds: consecutive barriers per workgroup, 1..64.
+ *   rounds: 1..64.  tags, seen: device u32 [W][rounds][nblocks] and
+ *   [W][rounds][nblocks][W] for the tag check described above, both NULL
+ *   for none; default launch only.
  * Errors: ARX_ESTATE, ARX_EINVAL, ARX_ETIMEOUT (latched), ARX_EHIP.
  */
-int arx_barrier_blockwise(int nblocks, int sem, int rounds, hipStream_t stream);
+int arx_barrier_blockwise(int nblocks, int sem, int rounds, int flags, uint32_t* tags, uint32_t* seen,
+                          hipStream_t stream);
 
 /*
  * arx_counter_barrier — the counter barrier and per-block epochs of page
  * "common.cuh" (Semaphore, PullController::sync, PushController) for the W
- * virtual ranks: launch `nblocks` workgroups of one wave; in workgroup b,
- * lanes [v*W, v*W + W) play rank v. Each workgroup records its epoch in
- * seen[b] (if seen is not NULL), runs `rounds` rounds of a start stage
- * (every rank adds 1 to block b's flag of every rank, the owner waits for
- * flag - base >= W) and a fenced end stage (waits for flag - base >= 2W,
- * then advances its base by 2W), then flips its epoch between 0 and 1.
- * Flags only grow: after R rounds in total, every flag and base of the
- * blocks used is 2 * W * R.
- *   nblocks: 1..ARX_MAX_PAD_BLOCKS.  rounds: 0..64.  seen: device u32
- *   [nblocks] or NULL.
+ * virtual ranks on block ids 0..nblocks-1. Each rank's block records its
+ * epoch in epochs_seen[v * nblocks + b] (if epochs_seen is not NULL), runs
+ * `rounds` rounds of a start stage (every rank adds 1 to block b's flag of
+ * every rank, the owner waits) and a fenced end stage (release adds, the
+ * owner's wait then an acquire), then flips its epoch between 0 and 1.
+ *   Page design (default): one flag per rank and block; the start stage
+ *   waits for flag - base >= W, the end stage for >= 2W and then advances
+ *   the base by 2W. Flags only grow: after R rounds in total every flag and
+ *   base of the blocks used is 2 * W * R. At W >= 3 over two or more rounds
+ *   an add from a rank a stage ahead (an unfenced start-stage add) can stand
+ *   in for a slow rank's end-stage add, so a rank can leave an end stage
+ *   without its acquire pairing with that slow rank's release.
+ *   flags & ARX_BARRIER_SPLIT (a repair, not the page's design): start
+ *   stages count on the semaphore's flag and base, end stages on its
+ *   end-stage pair; each stage waits for W and advances its base by W, so
+ *   every end stage pairs with every rank's release. After R rounds both
+ *   pairs are W * R.
+ *   Launch layouts as for arx_barrier_blockwise (default one workgroup per
+ *   rank and block, or ARX_BARRIER_LANES); the tag check writes each tag
+ *   between the start and the end stage and reads the peers' after the end
+ *   stage.
+ *   nblocks: 1..ARX_MAX_PAD_BLOCKS.  rounds: 0..64.  epochs_seen: device u32
+ *   [W][nblocks] or NULL.  tags, seen: as for arx_barrier_blockwise.
  * Errors: ARX_ESTATE, ARX_EINVAL, ARX_ETIMEOUT (latched), ARX_EHIP.
  */
-int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t stream);
+int arx_counter_barrier(int nblocks, int rounds, int flags, uint32_t* epochs_seen, uint32_t* tags, uint32_t* seen,
+                        hipStream_t stream);
 
 /*
  * arx_symm_allreduce — an all-reduce among the W virtual ranks of this GPU
@@ -184,20 +232,28 @@ int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t str
  *            starts at element (k * W + v) * ld.
  *   outputs: device bf16 [iters][W][ld], same layout; every rank's result.
  *   n <= max_n; ld >= n and a multiple of 8; both pointers 16-byte aligned;
- *   iters in [1, 65536]. Uses the signal pads (block ids 0..G-1) and the
+ *   iters in [1, 65536]; outputs == inputs (in place) or not overlapping it. Uses the signal pads (block ids 0..G-1) and the
  *   library's symmetric buffers [W][max_n], allocated by arx_init.
  * Errors: ARX_ESTATE, ARX_EINVAL, ARX_ETIMEOUT (latched), ARX_EHIP.
  */
 int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, int iters, hipStream_t stream);
 
+/* The largest nblocks the default launch (one workgroup per rank and block)
+ * of arx_barrier_blockwise and arx_counter_barrier accepts at this W: what
+ * the device holds at once divided by W, at most ARX_MAX_PAD_BLOCKS (0 if the
+ * occupancy query failed). The lane-group variant accepts
+ * ARX_MAX_PAD_BLOCKS. Errors: ARX_ESTATE. */
+int arx_barrier_max_blocks(void);
+
 /* Device address of rank `rank`'s semaphores: ARX_MAX_PAD_BLOCKS entries of
- * 32 u32 (128 bytes), flag at [0] and base at [1]; NULL if not initialised
- * or rank out of range. */
+ * 32 u32 (128 bytes): flag at [0] and base at [1], the split design's
+ * end-stage flag at [16] and base at [17]; NULL if not initialised or rank
+ * out of range. */
 const uint32_t* arx_sem_ptr(int rank);
 
-/* Device address of the per-block epochs, u32 [ARX_MAX_PAD_BLOCKS]; NULL if
- * not initialised. */
-const uint32_t* arx_epoch_ptr(void);
+/* Device address of rank `rank`'s per-block epochs, u32
+ * [ARX_MAX_PAD_BLOCKS]; NULL if not initialised or rank out of range. */
+const uint32_t* arx_epoch_ptr(int rank);
 
 /* Device address of recv slot [par][src] (max_n bf16), where the caller puts
  * peer src's partial for parity par; NULL if not initialised or out of range
@@ -240,37 +296,6 @@ int arx_set_timeout_us(uint64_t us);
  * published by this GPU, last seq posted for the peers, last seq whose
  * reduction finished. Any pointer may be NULL. */
 int arx_status(uint64_t* published, uint64_t* posted, uint64_t* done);
-
-/*
- * arx_debug_state — copy every protocol word, synchronously (waits for the
- * device), into words[0..nwords): [0] seq_dev, [1] arrival counter,
- * [2] finish counter, [3] go, [4] abort, [5] ctl.seq, [6] ctl.bytes[0],
- * [7] ctl.bytes[1], [8] ctl.done, [9] ctl.err, [10] ctl.err_seq,
- * [11] posted, [12 .. 12+W) flags[src]. seq_dev, ctl.seq, ctl.done, posted
- * abort and the flags are 64-bit sequence numbers; go holds the low 32 bits
- * of one. Returns the number of words written.
- */
-int arx_debug_state(uint64_t* words, int nwords);
-
-/* Test aid: set the protocol's state as if `seq` calls had completed
- * (device seq and go, ctl.seq, ctl.done, the proxy's posted seq and every
- * peer flag), so tests can reach large sequence numbers. Waits for the
- * device; allowed in the lockstep and manual modes only, with no call in
- * flight. Errors: ARX_ESTATE, ARX_EHIP. */
-int arx_debug_set_seq(uint64_t seq);
-
-/* Test aid: the proxy's next post in ARX_PROXY_STRESS mode fails, as a
- * failed copy of the peers' data would. The proxy thread then stops and the
- * failure is latched: the next arx_allreduce (or any call that launches)
- * returns ARX_EPROXY until arx_finalize, as the page's proxy error latch
- * makes the next all-reduce throw. A call already in flight never gets its
- * flags and ends through its bounded wait. Errors: ARX_ESTATE. */
-int arx_debug_fail_proxy(void);
-
-/* The binary32 -> bf16 rounding of the reduction alone (for exhaustive
- * checks): out[i] = the bf16 pattern the reduction writes for the binary32
- * pattern in[i]. in: device u32 [n], out: device u16 [n]; n <= 2^32 - 1. */
-int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream);
 
 /* Message for an error code; for the last failing call, the message includes
  * its detail (a HIP error string, the offending argument). */

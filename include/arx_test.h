@@ -1,0 +1,57 @@
+/*
+ * arx_test.h — test aids of libarx, exported beside the C ABI of arx.h but
+ * not part of the one-shot path: they read or set the protocol's state,
+ * force a proxy failure, and run the reduction's rounding alone, so that
+ * tests can check every protocol word, reach sequence numbers past 2^32,
+ * exercise the failure latch and compare the rounding exhaustively.
+ * Conventions (return codes, pointers, one instance per process) as in
+ * arx.h.
+ */
+#ifndef ARX_TEST_H
+#define ARX_TEST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * arx_debug_state — copy every protocol word, synchronously (waits for the
+ * device), into words[0..nwords): [0] seq_dev, [1] arrival counter,
+ * [2] finish counter, [3] go, [4] abort, [5] ctl.seq, [6] ctl.bytes[0],
+ * [7] ctl.bytes[1], [8] ctl.done, [9] ctl.err, [10] ctl.err_seq,
+ * [11] posted, [12 .. 12+W) flags[src]. seq_dev, ctl.seq, ctl.done, posted
+ * abort and the flags are 64-bit sequence numbers; go holds the low 32 bits
+ * of one. Returns the number of words written.
+ */
+int arx_debug_state(uint64_t* words, int nwords);
+
+/* Test aid: set the protocol's state as if `seq` calls had completed
+ * (device seq and go, ctl.seq, ctl.done, the proxy's posted seq and every
+ * peer flag), so tests can reach large sequence numbers. Waits for the
+ * device; allowed in the lockstep and manual modes only, with no call in
+ * flight. Errors: ARX_ESTATE, ARX_EHIP. */
+int arx_debug_set_seq(uint64_t seq);
+
+/* Test aid: the proxy's next post in ARX_PROXY_STRESS mode fails, as a
+ * failed copy of the peers' data would. The proxy thread then stops and the
+ * failure is latched: the next arx_allreduce (or any call that launches)
+ * returns ARX_EPROXY until arx_finalize, as the page's proxy error latch
+ * makes the next all-reduce throw. A call already in flight never gets its
+ * flags and ends through its bounded wait. Errors: ARX_ESTATE. */
+int arx_debug_fail_proxy(void);
+
+/* The binary32 -> bf16 rounding of the reduction alone (for exhaustive
+ * checks): out[i] = the bf16 pattern the reduction writes for the binary32
+ * pattern in[i]. in: device u32 [n], out: device u16 [n]; n <= 2^32 - 1. */
+int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARX_TEST_H */

@@ -105,13 +105,15 @@ def _post(st: ProtocolState, s: int) -> None:
 
 def sequential_model(calls: Sequence[Tuple[np.ndarray, int]], recv, W: int, rank: int = 0,
                      max_n: Optional[int] = None, mode: str = LOCKSTEP,
-                     state: Optional[ProtocolState] = None):
+                     state: Optional[ProtocolState] = None, threads: int = 1):
     """Runs the calls (each ``(in_bits, n)``) through the one-shot path in order.
 
     recv[par][src] holds peer src's partial for parity par. Returns
     ``(state, outs)`` where outs[k] holds the first n elements of call k's
     output. In MANUAL mode no flags are posted, so a call whose flags are
-    missing raises (the GPU would wait for them).
+    missing raises (the GPU would wait for them). threads: host threads of
+    each call's reduction (contiguous index ranges; the same bits for any
+    count).
     """
     if max_n is None:
         max_n = max((n for _, n in calls), default=0)
@@ -135,7 +137,7 @@ def sequential_model(calls: Sequence[Tuple[np.ndarray, int]], recv, W: int, rank
             raise RuntimeError(f"seq {seq}: a peer flag never reached seq (flags {st.flags})")
         st.go = seq & U32                  # workgroup 0 releases the others
         parts = [st.send[par] if src == rank else recv[par][src] for src in range(W)]
-        outs.append(_reduce.reduce(parts, n=n))
+        outs.append(_reduce.reduce(parts, n=n, threads=threads))
         st.seq_dev = seq                   # last block out
         st.ctl_done = seq
     return st, outs
@@ -379,12 +381,21 @@ BARRIER_MUTANTS = {
     None: "CAS 0->1 to signal, CAS 1->0 to consume (page triton_barrier.py)",
     "B1": "signal with a plain store of 1 instead of a CAS from 0",
     "B2": "wait reads the 1 without clearing it",
+    "B3": "the peers' tags are read once this rank's signals are sent, before it consumes theirs",
 }
 
 
 def check_barrier(W: int, K: int, mutant: Optional[str] = None,
                   max_states: int = 5_000_000) -> CheckResult:
     """Explores every interleaving of W ranks' lanes over K barrier rounds.
+
+    Tags: on entering round k a rank writes its tag for round k (before any
+    of its lanes signals, as the workgroup barrier of the page's usage
+    pattern 1 orders it), and on leaving round k it reads every rank's tag
+    for round k; the read must find it written. A rank has written its
+    round-k tag exactly when it has entered round k, so this is the check
+    that no rank leaves a round before every rank entered it. Mutant B3 moves
+    the read to the moment this rank's last signal is sent.
 
     State: (rounds, lanes, pad). rounds[r] = rounds rank r has entered
     (1..K, K + 1 once finished); lanes[r*W+s] = lane s's step in rank r's
@@ -412,7 +423,14 @@ def check_barrier(W: int, K: int, mutant: Optional[str] = None,
                     pi = s * W + r          # slot r of rank s's pad
                     if mutant == "B1" or pad[pi] == 0:
                         pad2 = pad[:pi] + (1,) + pad[pi + 1:]
-                        succ.append((rounds, lanes[:li] + (WAITSIG,) + lanes[li + 1:], pad2))
+                        lanes2 = lanes[:li] + (WAITSIG,) + lanes[li + 1:]
+                        if mutant == "B3" and all(lanes2[r * W + x] != SEND for x in range(W)):
+                            k = rounds[r]
+                            for q in range(W):
+                                if rounds[q] < k:
+                                    return CheckResult(False, len(seen), (
+                                        f"rank {r} read rank {q}'s round-{k} tag before rank {q} wrote it"))
+                        succ.append((rounds, lanes2, pad2))
                 elif step == WAITSIG:
                     pi = r * W + s          # slot s of this rank's pad
                     if pad[pi] == 1:
@@ -421,11 +439,12 @@ def check_barrier(W: int, K: int, mutant: Optional[str] = None,
                         succ.append((rounds, lanes2, pad2))
             if all(lanes[r * W + s] == LANEDONE for s in range(W)):
                 k = rounds[r]
-                # rank r leaves round k: every rank must have entered round k
+                # rank r leaves round k and reads every rank's round-k tag:
+                # every rank must have entered round k (written that tag)
                 for q in range(W):
-                    if rounds[q] < k:
+                    if rounds[q] < k and mutant != "B3":
                         return CheckResult(False, len(seen), (
-                            f"rank {r} left round {k} before rank {q} entered it"))
+                            f"rank {r} left round {k} before rank {q} entered it (read an unwritten tag)"))
                 nxt = (SEND,) if k + 1 <= K else (LANEDONE,)
                 rounds2 = rounds[:r] + (k + 1,) + rounds[r + 1:]
                 lanes2 = lanes[:r * W] + nxt * W + lanes[r * W + W:]
@@ -448,6 +467,36 @@ def check_barrier(W: int, K: int, mutant: Optional[str] = None,
                 if len(seen) > max_states:
                     raise RuntimeError(f"state space exceeds {max_states}")
     return CheckResult(True, len(seen), None, finals)
+
+
+def barrier_tag(rank: int, block: int, rnd: int) -> int:
+    """The tag rank `rank`'s workgroup for block `block` writes before round
+    `rnd` of a tagged barrier launch: 0x80000000 | rnd << 16 | block << 4 |
+    rank (the library's documented tag format)."""
+    return 0x80000000 | (rnd << 16) | (block << 4) | rank
+
+
+def barrier_tags_written(W: int, nblocks: int, rounds: int) -> np.ndarray:
+    """The tag rows after a tagged launch, u32 [W, rounds, nblocks]: rank v's
+    slot for round r and block b holds barrier_tag(v, b, r)."""
+    out = np.zeros((W, rounds, nblocks), np.uint32)
+    for v in range(W):
+        for r in range(rounds):
+            for b in range(nblocks):
+                out[v, r, b] = barrier_tag(v, b, r)
+    return out
+
+
+def barrier_tags_seen(W: int, nblocks: int, rounds: int) -> np.ndarray:
+    """What a tagged barrier launch reads back, u32 [W, rounds, nblocks, W]:
+    after round r, rank v's block b reads rank p's round-r tag for block b.
+    check_barrier shows that every rank has written it by then (no rank
+    leaves a round before every rank entered it), and the acquire / release
+    pairing of each signal makes the write visible, so the read returns
+    barrier_tag(p, b, r) for every p (page "triton_barrier.py",
+    blockwise_barrier docstring, usage pattern 1)."""
+    written = barrier_tags_written(W, nblocks, rounds)       # [p, r, b]
+    return np.broadcast_to(np.transpose(written, (1, 2, 0))[None], (W, rounds, nblocks, W)).copy()
 
 
 def barrier_pads_after(W: int, nblocks: int, rounds: int = 1) -> List[np.ndarray]:

@@ -1,4 +1,5 @@
-"""ctypes binding of libarx.so (C ABI in include/arx.h).
+"""ctypes binding of libarx.so (C ABI in include/arx.h, test aids in
+include/arx_test.h).
 
 Argument marshalling only: every step of the path runs in the library's HIP
 kernels. torch provides device memory and streams; tensors are passed as
@@ -14,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarx.so")
 OK, EINVAL, ESTATE, ENOMEM, EHIP, EPROXY, EORDER, ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7
 PROXY_LOCKSTEP, PROXY_RUNAHEAD, PROXY_MANUAL, PROXY_STRESS = 0, 1, 2, 3
 SEM_RELAXED, SEM_ACQ_REL = 0, 1
+BARRIER_LANES, BARRIER_SPLIT = 1, 2
 MAX_WORLD, MAX_PAD_BLOCKS, MAX_N = 8, 1024, 1 << 30
 
 # names of arx_debug_state's words, in order
@@ -23,7 +25,7 @@ STATE_WORDS = ["seq_dev", "cnt0", "cnt1", "go", "abort", "ctl_seq", "ctl_bytes0"
 _c = ctypes
 _u64p = _c.POINTER(_c.c_uint64)
 
-# (name, restype, argtypes) for every entry point of arx.h
+# (name, restype, argtypes) for every entry point of arx.h and arx_test.h
 SIGNATURES = [
     ("arx_init", _c.c_int, [_c.c_int, _c.c_size_t]),
     ("arx_init_rank", _c.c_int, [_c.c_int, _c.c_size_t, _c.c_int]),
@@ -31,11 +33,14 @@ SIGNATURES = [
     ("arx_publish", _c.c_int, [_c.c_uint64]),
     ("arx_allreduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     ("arx_reduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_void_p]),
-    ("arx_barrier_blockwise", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
-    ("arx_counter_barrier", _c.c_int, [_c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p]),
+    ("arx_barrier_blockwise", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                         _c.c_void_p]),
+    ("arx_counter_barrier", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                       _c.c_void_p]),
     ("arx_symm_allreduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_size_t, _c.c_int, _c.c_void_p]),
+    ("arx_barrier_max_blocks", _c.c_int, []),
     ("arx_sem_ptr", _c.c_void_p, [_c.c_int]),
-    ("arx_epoch_ptr", _c.c_void_p, []),
+    ("arx_epoch_ptr", _c.c_void_p, [_c.c_int]),
     ("arx_recv_ptr", _c.c_void_p, [_c.c_int, _c.c_int]),
     ("arx_send_ptr", _c.c_void_p, [_c.c_int]),
     ("arx_pad_ptr", _c.c_void_p, [_c.c_int]),
@@ -146,14 +151,38 @@ def reduce(inp, out, par: int, n: int = None, stream=None):
     _check(lib.arx_reduce(_buf(inp, n, "inp"), _buf(out, n, "out"), n, par, _stream(stream)))
 
 
-def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, stream=None):
-    _check(lib.arx_barrier_blockwise(nblocks, sem, rounds, _stream(stream)))
+def _tag_bufs(tags, seen, rounds: int, nblocks: int):
+    """Addresses of a tag check's buffers: tags u32 [W, rounds, nblocks] and
+    seen u32 [W, rounds, nblocks, W], both given or neither."""
+    if tags is None and seen is None:
+        return None, None
+    if tags is None or seen is None:
+        raise ArxError(EINVAL, "tags and seen go together")
+    W = world()
+    return _buf(tags, W * rounds * nblocks, "tags", 4), _buf(seen, W * rounds * nblocks * W, "seen", 4)
 
 
-def counter_barrier(nblocks: int, rounds: int = 1, seen=None, stream=None):
-    """seen: optional int32 device tensor [nblocks] receiving each block's epoch."""
-    ptr = None if seen is None else _buf(seen, nblocks, "seen", 4)
-    _check(lib.arx_counter_barrier(nblocks, rounds, ptr, _stream(stream)))
+def barrier_blockwise(nblocks: int, sem: int = SEM_ACQ_REL, rounds: int = 1, flags: int = 0, tags=None, seen=None,
+                      stream=None):
+    """W * nblocks workgroups (or nblocks with flags=BARRIER_LANES) pass the
+    blockwise barrier `rounds` times; tags / seen: int32 device tensors for
+    the tag check (arx.h, barrier tags)."""
+    tp, sp = _tag_bufs(tags, seen, rounds, nblocks)
+    _check(lib.arx_barrier_blockwise(nblocks, sem, rounds, flags, tp, sp, _stream(stream)))
+
+
+def counter_barrier(nblocks: int, rounds: int = 1, flags: int = 0, epochs_seen=None, tags=None, seen=None,
+                    stream=None):
+    """epochs_seen: optional int32 device tensor [W, nblocks] receiving each
+    rank's block's epoch; tags / seen as for barrier_blockwise."""
+    ptr = None if epochs_seen is None else _buf(epochs_seen, world() * nblocks, "epochs_seen", 4)
+    tp, sp = _tag_bufs(tags, seen, rounds, nblocks)
+    _check(lib.arx_counter_barrier(nblocks, rounds, flags, ptr, tp, sp, _stream(stream)))
+
+
+def barrier_max_blocks() -> int:
+    """Largest nblocks of a barrier launch with one workgroup per rank and block."""
+    return _check(lib.arx_barrier_max_blocks())
 
 
 def symm_allreduce(inputs, outputs, n: int, iters: int, stream=None):
@@ -168,13 +197,14 @@ def symm_allreduce(inputs, outputs, n: int, iters: int, stream=None):
 
 def sem_view(rank: int):
     """int32 tensor viewing rank `rank`'s semaphores, shape [MAX_PAD_BLOCKS, 32]
-    (flag in column 0, base in column 1)."""
+    (flag in column 0, base in column 1; the split design's end-stage flag in
+    column 16, its base in column 17)."""
     return _view(lib.arx_sem_ptr(rank), MAX_PAD_BLOCKS * 32, "<i4", None).view(MAX_PAD_BLOCKS, 32)
 
 
-def epoch_view():
-    """int32 tensor viewing the per-block epochs, shape [MAX_PAD_BLOCKS]."""
-    return _view(lib.arx_epoch_ptr(), MAX_PAD_BLOCKS, "<i4", None)
+def epoch_view(rank: int):
+    """int32 tensor viewing rank `rank`'s per-block epochs, shape [MAX_PAD_BLOCKS]."""
+    return _view(lib.arx_epoch_ptr(rank), MAX_PAD_BLOCKS, "<i4", None)
 
 
 def set_proxy_mode(mode: int):

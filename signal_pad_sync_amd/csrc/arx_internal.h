@@ -78,16 +78,23 @@ struct BarrierArgs {
   int world;
   int acq_rel;
   int rounds;
+  int nblocks;
+  uint32_t* tags;      // [W][rounds][nblocks] barrier tags written (or null)
+  uint32_t* seen;      // [W][rounds][nblocks][W] tags read back after each round (or null)
   uint64_t timeout;
   Ctl* ctl;
 };
 
 struct CounterArgs {
   Semaphore* sem[8];   // rank r's semaphores, one per block id
-  uint32_t* epochs;    // one per block id
-  uint32_t* seen;      // seen[b] = the epoch block b read (for checks), or null
+  uint32_t* epochs[8]; // rank r's epochs, one per block id
+  uint32_t* seen;      // [W][nblocks]: the epoch each rank's block read (for checks), or null
+  uint32_t* tags;      // [W][rounds][nblocks] barrier tags written before each end stage (or null)
+  uint32_t* tag_seen;  // [W][rounds][nblocks][W] tags read back after each end stage (or null)
   int world;
   int rounds;
+  int nblocks;
+  int split;           // separate start- and end-stage semaphores
   uint64_t timeout;
   Ctl* ctl;
 };
@@ -114,8 +121,13 @@ struct SymmArgs {
 hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, int cus, hipStream_t stream);
 int oneshot_block(uint32_t n);
 hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t stream);
-hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t stream);
-hipError_t launch_counter_barrier(const CounterArgs& a, int nblocks, hipStream_t stream);
+// The barrier launchers: lanes = true puts block b of every rank in one wave
+// (nblocks workgroups), false gives rank v's block b a workgroup of its own
+// (world * nblocks workgroups, which must all be resident at once:
+// barrier_groups_cap gives the most the device holds, 0 if unknown).
+hipError_t launch_barrier(const BarrierArgs& a, bool lanes, hipStream_t stream);
+hipError_t launch_counter_barrier(const CounterArgs& a, bool lanes, hipStream_t stream);
+long long barrier_groups_cap(bool counter, int cus);
 hipError_t launch_symm_allreduce(const SymmArgs& a, hipStream_t stream);
 int symm_blocks(uint32_t n, int world, int cus);
 hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t stream);

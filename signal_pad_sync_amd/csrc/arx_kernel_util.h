@@ -5,7 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "arx_device.h"
+#include "arx_prims.h"
 #include "arx_internal.h"
 
 namespace arx {

@@ -1,4 +1,4 @@
-// arx_device.h — device-side building blocks of libarx for gfx950 (HIP).
+// arx_prims.h — device-side building blocks of libarx for gfx950 (HIP).
 //
 // Memory-scope vocabulary used throughout (HIP / LLVM AMDGPU memory model):
 //   agent  = every workgroup of this GPU, across its 8 XCDs (each XCD has its
@@ -37,37 +37,43 @@ template <typename T>
 __device__ __forceinline__ void store_relaxed_system(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+// Releases. A release fence writes the issuing XCD's L2 back (buffer_wbl2)
+// and must wait for that write-back to finish before the releasing access
+// is issued, or the access can reach memory ahead of the data it publishes.
+// The compiler emits that wait as a relaxable one, and merges it away when an
+// earlier wait has already drained the counters (seen on gfx950 for a
+// release atomic issued right after a load it needed: buffer_wbl2 followed
+// directly by the atomic). So every release here is an explicit fence, then
+// a hard wait for all outstanding memory operations (s_waitcnt 0), then a
+// relaxed access.
+__device__ __forceinline__ void fence_release_system() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+  __builtin_amdgcn_s_waitcnt(0);
+}
+__device__ __forceinline__ void fence_release_agent() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __builtin_amdgcn_s_waitcnt(0);
+}
 template <typename T>
 __device__ __forceinline__ void store_release_agent(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  fence_release_agent();
+  store_relaxed_agent(p, v);
 }
 template <typename T>
 __device__ __forceinline__ void store_release_system(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  fence_release_system();
+  store_relaxed_system(p, v);
 }
 __device__ __forceinline__ uint32_t fetch_add_release_system(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  fence_release_system();
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 __device__ __forceinline__ uint32_t fetch_add_relaxed_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void fence_acquire_system() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, ""); }
-__device__ __forceinline__ void fence_release_system() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, ""); }
 __device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-// Compare-and-swap at system scope; returns true if *p held `expect` and now
-// holds `desired`. Failure ordering is relaxed (a failed attempt is retried).
-__device__ __forceinline__ bool cas_system(uint32_t* p, uint32_t expect, uint32_t desired, int order) {
-  if (order == __ATOMIC_RELEASE)
-    return __hip_atomic_compare_exchange_strong(p, &expect, desired, __ATOMIC_RELEASE, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_SYSTEM);
-  if (order == __ATOMIC_ACQUIRE)
-    return __hip_atomic_compare_exchange_strong(p, &expect, desired, __ATOMIC_ACQUIRE, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_SYSTEM);
-  return __hip_atomic_compare_exchange_strong(p, &expect, desired, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_SYSTEM);
-}
 
 // Constant-rate clock (the wall clock; its rate is a device attribute).
 __device__ __forceinline__ uint64_t now_ticks() { return (uint64_t)wall_clock64(); }

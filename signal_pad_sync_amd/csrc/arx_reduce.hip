@@ -14,7 +14,7 @@
 // bytes per instruction.
 #include <hip/hip_runtime.h>
 
-#include "arx_device.h"
+#include "arx_prims.h"
 #include "arx_internal.h"
 #include "arx_kernel_util.h"
 
@@ -87,9 +87,10 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
     }
   }
 
-  // 3. workgroup 0 waits for every peer's flag to reach seq, then releases
-  //    the other workgroups through the go word; they wait on go only, so
-  //    just a few lanes poll the pinned flags over PCIe
+  // 3. flag wait and go broadcast (page "arx.cu", protocol comment): W - 1
+  //    lanes of workgroup 0 poll the pinned flags over PCIe until each holds
+  //    seq or more; workgroup 0 then stores seq into the device's go word,
+  //    which is all the other workgroups poll
   bool abort;
   if (blockIdx.x == 0) {
     bool ok = true;

@@ -1,5 +1,6 @@
 // arx_runtime.cpp — host side of libarx: state, the proxy thread that posts
-// the virtual peers' flags, argument checks and the C ABI declared in arx.h.
+// the virtual peers' flags, argument checks and the C ABI declared in arx.h
+// and arx_test.h.
 //
 // Page "arx.cu": arx_prepare / arx_connect allocate and zero the pinned and
 // device state and start the proxy; arx_allreduce checks its arguments and
@@ -18,6 +19,7 @@
 #include <thread>
 
 #include "arx.h"
+#include "arx_test.h"
 #include "arx_internal.h"
 #include "arx_sync.h"
 #include "arx_proxy.h"
@@ -38,7 +40,7 @@ struct State {
   uint16_t* recv = nullptr;   // device [2][W][stride]
   uint32_t* pads = nullptr;   // device [W][ARX_MAX_PAD_BLOCKS][W]
   arx::Semaphore* sems = nullptr;  // device [W][ARX_MAX_PAD_BLOCKS]
-  uint32_t* epochs = nullptr;      // device [ARX_MAX_PAD_BLOCKS]
+  uint32_t* epochs = nullptr;      // device [W][ARX_MAX_PAD_BLOCKS]
   uint16_t* symm = nullptr;        // device [W][stride]: the virtual ranks' symmetric buffers
   uint32_t* words = nullptr;  // device [WORDS_TOTAL]
   Ctl* ctl = nullptr;         // pinned, host address
@@ -167,7 +169,7 @@ int init_impl(int world, size_t max_n, int rank) {
   const size_t pads_b = (size_t)world * ARX_MAX_PAD_BLOCKS * world * sizeof(uint32_t);
   const size_t words_b = arx::WORDS_TOTAL * sizeof(uint32_t);
   const size_t sems_b = (size_t)world * ARX_MAX_PAD_BLOCKS * sizeof(arx::Semaphore);
-  const size_t epochs_b = ARX_MAX_PAD_BLOCKS * sizeof(uint32_t);
+  const size_t epochs_b = (size_t)world * ARX_MAX_PAD_BLOCKS * sizeof(uint32_t);
   const size_t symm_b = (size_t)world * S.stride * sizeof(uint16_t);
   int rc = ARX_OK;
   hipError_t e;
@@ -215,10 +217,36 @@ int init_impl(int world, size_t max_n, int rank) {
   return ARX_OK;
 }
 
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
 int check_ptrs(const void* in, const void* out, size_t n) {
   if (n > S.max_n) return fail(ARX_EINVAL, "n %zu exceeds max_n %zu", n, S.max_n);
   if (n > 0 && (in == nullptr || out == nullptr)) return fail(ARX_EINVAL, "null in or out");
   if (((uintptr_t)in & 15u) || ((uintptr_t)out & 15u)) return fail(ARX_EINVAL, "in and out must be 16-byte aligned");
+  if (in != out && overlap(in, 2 * n, out, 2 * n))
+    return fail(ARX_EINVAL, "in and out overlap without being the same buffer");
+  return ARX_OK;
+}
+
+// The tag buffers of a barrier launch: both given or neither, and only with
+// one workgroup per rank and block.
+int check_tags(const uint32_t* tags, const uint32_t* seen, bool lanes) {
+  if ((tags == nullptr) != (seen == nullptr)) return fail(ARX_EINVAL, "tags and seen go together");
+  if (tags && lanes) return fail(ARX_EINVAL, "tags need one workgroup per rank and block (no ARX_BARRIER_LANES)");
+  return ARX_OK;
+}
+
+// A launch of world * nblocks workgroups that wait on each other must fit on
+// the device at once.
+int check_groups(int nblocks, bool counter) {
+  const long long cap = arx::barrier_groups_cap(counter, S.cus);
+  if ((long long)S.world * nblocks > cap)
+    return fail(ARX_EINVAL, "%d workgroups (W %d x nblocks %d) exceed the %lld the device holds at once",
+                S.world * nblocks, S.world, nblocks, cap);
   return ARX_OK;
 }
 
@@ -291,40 +319,59 @@ int arx_reduce(const void* in, void* out, size_t n, int par, hipStream_t stream)
   return ARX_OK;
 }
 
-int arx_barrier_blockwise(int nblocks, int sem, int rounds, hipStream_t stream) {
+int arx_barrier_blockwise(int nblocks, int sem, int rounds, int flags, uint32_t* tags, uint32_t* seen,
+                          hipStream_t stream) {
   int rc = check_ready();
   if (rc != ARX_OK) return rc;
   if (nblocks < 1 || nblocks > ARX_MAX_PAD_BLOCKS)
     return fail(ARX_EINVAL, "nblocks %d not in [1, %d]", nblocks, ARX_MAX_PAD_BLOCKS);
   if (sem != ARX_SEM_RELAXED && sem != ARX_SEM_ACQ_REL) return fail(ARX_EINVAL, "sem %d unknown", sem);
   if (rounds < 1 || rounds > 64) return fail(ARX_EINVAL, "rounds %d not in [1, 64]", rounds);
+  if (flags & ~ARX_BARRIER_LANES) return fail(ARX_EINVAL, "barrier flags %#x unknown", flags);
+  const bool lanes = (flags & ARX_BARRIER_LANES) != 0;
+  if ((rc = check_tags(tags, seen, lanes)) != ARX_OK) return rc;
+  if (!lanes && (rc = check_groups(nblocks, false)) != ARX_OK) return rc;
   arx::BarrierArgs a;
   for (int i = 0; i < 8; ++i)
     a.pad[i] = i < S.world ? S.pads + (size_t)i * ARX_MAX_PAD_BLOCKS * S.world : nullptr;
   a.world = S.world;
   a.acq_rel = sem == ARX_SEM_ACQ_REL;
   a.rounds = rounds;
+  a.nblocks = nblocks;
+  a.tags = tags;
+  a.seen = seen;
   a.timeout = timeout_ticks();
   a.ctl = S.ctl_dev;
-  HIPCHK(arx::launch_barrier(a, nblocks, stream));
+  HIPCHK(arx::launch_barrier(a, lanes, stream));
   return ARX_OK;
 }
 
-int arx_counter_barrier(int nblocks, int rounds, uint32_t* seen, hipStream_t stream) {
+int arx_counter_barrier(int nblocks, int rounds, int flags, uint32_t* epochs_seen, uint32_t* tags, uint32_t* seen,
+                        hipStream_t stream) {
   int rc = check_ready();
   if (rc != ARX_OK) return rc;
   if (nblocks < 1 || nblocks > ARX_MAX_PAD_BLOCKS)
     return fail(ARX_EINVAL, "nblocks %d not in [1, %d]", nblocks, ARX_MAX_PAD_BLOCKS);
   if (rounds < 0 || rounds > 64) return fail(ARX_EINVAL, "rounds %d not in [0, 64]", rounds);
+  if (flags & ~(ARX_BARRIER_LANES | ARX_BARRIER_SPLIT)) return fail(ARX_EINVAL, "barrier flags %#x unknown", flags);
+  const bool lanes = (flags & ARX_BARRIER_LANES) != 0;
+  if ((rc = check_tags(tags, seen, lanes)) != ARX_OK) return rc;
+  if (!lanes && (rc = check_groups(nblocks, true)) != ARX_OK) return rc;
   arx::CounterArgs a;
-  for (int i = 0; i < 8; ++i) a.sem[i] = i < S.world ? S.sems + (size_t)i * ARX_MAX_PAD_BLOCKS : nullptr;
-  a.epochs = S.epochs;
-  a.seen = seen;
+  for (int i = 0; i < 8; ++i) {
+    a.sem[i] = i < S.world ? S.sems + (size_t)i * ARX_MAX_PAD_BLOCKS : nullptr;
+    a.epochs[i] = i < S.world ? S.epochs + (size_t)i * ARX_MAX_PAD_BLOCKS : nullptr;
+  }
+  a.seen = epochs_seen;
+  a.tags = tags;
+  a.tag_seen = seen;
   a.world = S.world;
   a.rounds = rounds;
+  a.nblocks = nblocks;
+  a.split = (flags & ARX_BARRIER_SPLIT) != 0;
   a.timeout = timeout_ticks();
   a.ctl = S.ctl_dev;
-  HIPCHK(arx::launch_counter_barrier(a, nblocks, stream));
+  HIPCHK(arx::launch_counter_barrier(a, lanes, stream));
   return ARX_OK;
 }
 
@@ -337,6 +384,9 @@ int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, i
   if (n > 0 && (inputs == nullptr || outputs == nullptr)) return fail(ARX_EINVAL, "null inputs or outputs");
   if (((uintptr_t)inputs & 15u) || ((uintptr_t)outputs & 15u))
     return fail(ARX_EINVAL, "inputs and outputs must be 16-byte aligned");
+  const size_t extent = (size_t)iters * S.world * ld * sizeof(uint16_t);
+  if (inputs != outputs && overlap(inputs, extent, outputs, extent))
+    return fail(ARX_EINVAL, "inputs and outputs overlap without being the same buffer");
   arx::SymmArgs a;
   a.inputs = (const uint16_t*)inputs;
   a.outputs = (uint16_t*)outputs;
@@ -355,12 +405,22 @@ int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, i
   return ARX_OK;
 }
 
+int arx_barrier_max_blocks(void) {
+  if (!S.inited) return fail(ARX_ESTATE, "arx is not initialised");
+  const long long a = arx::barrier_groups_cap(false, S.cus), b = arx::barrier_groups_cap(true, S.cus);
+  const long long most = (a < b ? a : b) / S.world;
+  return (int)(most < ARX_MAX_PAD_BLOCKS ? most : ARX_MAX_PAD_BLOCKS);
+}
+
 const uint32_t* arx_sem_ptr(int rank) {
   if (!S.inited || rank < 0 || rank >= S.world) return nullptr;
   return reinterpret_cast<const uint32_t*>(S.sems + (size_t)rank * ARX_MAX_PAD_BLOCKS);
 }
 
-const uint32_t* arx_epoch_ptr(void) { return S.inited ? S.epochs : nullptr; }
+const uint32_t* arx_epoch_ptr(int rank) {
+  if (!S.inited || rank < 0 || rank >= S.world) return nullptr;
+  return S.epochs + (size_t)rank * ARX_MAX_PAD_BLOCKS;
+}
 
 void* arx_recv_ptr(int par, int src) {
   if (!S.inited || (par != 0 && par != 1) || src < 0 || src >= S.world) return nullptr;

@@ -1,14 +1,17 @@
 // arx_sync.hip — the synchronisation kernels of libarx for gfx950, each for
 // W virtual ranks on this GPU:
-//   barrier_kernel           the blockwise signal-pad barrier (page
-//                            "triton_barrier.py", blockwise_barrier)
-//   counter_barrier_kernel   the counter barrier and per-block epochs (page
+//   barrier_groups_kernel    the blockwise signal-pad barrier (page
+//                            "triton_barrier.py", blockwise_barrier), one
+//                            workgroup per rank and block
+//   barrier_lanes_kernel     the same, the W ranks as lane groups of a wave
+//   counter_groups_kernel    the counter barrier and per-block epochs (page
 //                            "common.cuh", PullController, PushController)
+//   counter_lanes_kernel     the same, as lane groups
 //   symm_allreduce_kernel    an all-reduce through symmetric buffers fenced
 //                            by the pad barrier's usage patterns
 #include <hip/hip_runtime.h>
 
-#include "arx_device.h"
+#include "arx_prims.h"
 #include "arx_internal.h"
 #include "arx_kernel_util.h"
 #include "arx_sync.h"
@@ -17,26 +20,53 @@ namespace arx {
 
 // ---- blockwise signal-pad barrier for W virtual ranks ----------------------
 
-// Workgroup b is one wave; its lanes [v * W, v * W + W) play virtual rank v,
-// lane v * W + s being that rank's lane s, and call the barrier on block id b
-// `rounds` times. A wave runs its lanes' signal loop to completion before
-// their consume loop, so every consume finds its signal and no lane waits on
-// a lane that has not run. One wave per rank group also means one release
-// and one acquire fence per workgroup, not one per virtual rank. With acq_rel
-// each round follows usage pattern 1 of the page (workgroup barrier, acq_rel
-// barrier, workgroup barrier); relaxed rounds follow pattern 0. The timeout
-// only guards against pads that were not zero-filled.
-__global__ __launch_bounds__(64) void barrier_kernel(BarrierArgs a) {
+// One workgroup per rank and block (the default launch): workgroup g plays
+// rank v = g % W's block b = g / W, so the W workgroups that synchronise on
+// block id b are consecutive and the dispatcher deals them to different XCDs
+// (workgroups go round robin to the 8 XCDs), whose L2 caches are not shared:
+// a missing release or acquire shows up as a stale tag. Each round follows
+// the page's usage pattern 1 with acq_rel (workgroup barrier, barrier,
+// workgroup barrier) and pattern 0 with relaxed. With tags, thread 0 writes
+// this block's tag for the round into rank v's tag row before the barrier,
+// and after it thread p < W reads rank p's tag for the same block and round
+// into seen; each round has tag slots of its own, so nothing is overwritten
+// while a peer may still read it.
+__global__ __launch_bounds__(64) void barrier_groups_kernel(BarrierArgs a) {
+  const int W = a.world;
+  const int v = (int)(blockIdx.x % (uint32_t)W);
+  const uint32_t b = blockIdx.x / (uint32_t)W;
+  const size_t nb = (size_t)a.nblocks;
+  for (int r = 0; r < a.rounds; ++r) {
+    if (a.tags && threadIdx.x == 0) a.tags[((size_t)v * a.rounds + r) * nb + b] = barrier_tag(v, b, r);
+    if (a.acq_rel) __syncthreads();
+    const bool ok = arx_detail::barrier_lane(a.pad, W, v, b, (int)threadIdx.x, a.acq_rel != 0, a.timeout);
+    if (__syncthreads_or(!ok)) {
+      if (threadIdx.x == 0) report_error(a.ctl, ERR_BARRIER_TIMEOUT, (uint64_t)blockIdx.x);
+      return;
+    }
+    if (a.seen && (int)threadIdx.x < W)
+      a.seen[(((size_t)v * a.rounds + r) * nb + b) * W + threadIdx.x] =
+          a.tags[((size_t)threadIdx.x * a.rounds + r) * nb + b];
+  }
+}
+
+// Lane groups (the named variant): workgroup b is one wave whose lanes
+// [v * W, v * W + W) play virtual rank v, lane v * W + s being that rank's
+// lane s, and call the barrier on block id b `rounds` times. A wave runs its
+// lanes' signal loop to completion before their consume loop, so every
+// consume finds its signal and no workgroup waits on another: this launch
+// measures the barrier's atomics and fences without cross-workgroup waiting.
+__global__ __launch_bounds__(64) void barrier_lanes_kernel(BarrierArgs a) {
   const int W = a.world;
   const int t = threadIdx.x;
   const int v = t / W, s = t - v * W;
   const bool active = t < W * W;
   const size_t row = (size_t)blockIdx.x * W;
-  uint32_t* const send_slot = select_pad(a.pad, s) + row + v;   // slot v of rank s's pad
-  uint32_t* const wait_slot = select_pad(a.pad, v) + row + s;   // slot s of rank v's pad
+  uint32_t* const send_slot = arx_detail::select_pad(a.pad, s) + row + v;   // slot v of rank s's pad
+  uint32_t* const wait_slot = arx_detail::select_pad(a.pad, v) + row + s;   // slot s of rank v's pad
   for (int r = 0; r < a.rounds; ++r) {
     if (a.acq_rel) __syncthreads();
-    const bool ok = !active || barrier_signal_wait(send_slot, wait_slot, a.acq_rel != 0, a.timeout);
+    const bool ok = !active || arx_detail::signal_wait(send_slot, wait_slot, a.acq_rel != 0, a.timeout);
     if (__syncthreads_or(!ok)) {
       if (threadIdx.x == 0) report_error(a.ctl, ERR_BARRIER_TIMEOUT, (uint64_t)blockIdx.x);
       return;
@@ -44,44 +74,108 @@ __global__ __launch_bounds__(64) void barrier_kernel(BarrierArgs a) {
   }
 }
 
-hipError_t launch_barrier(const BarrierArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL(barrier_kernel, dim3(nblocks), dim3(64), 0, s, a);
+hipError_t launch_barrier(const BarrierArgs& a, bool lanes, hipStream_t s) {
+  if (lanes) hipLaunchKernelGGL(barrier_lanes_kernel, dim3(a.nblocks), dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(barrier_groups_kernel, dim3(a.world * a.nblocks), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 // ---- counter barrier and per-block epochs for W virtual ranks -------------
 
-// Workgroup b is one wave; lanes [v * W, v * W + W) play virtual rank v. The
-// block reads its epoch first, runs `rounds` rounds of a start stage
-// (unfenced) and an end stage (fenced) on block id b as the page's
-// PullController does, then flips its epoch as PushController::exit does.
-__global__ __launch_bounds__(64) void counter_barrier_kernel(CounterArgs a) {
+// One round: a start stage (unfenced) then an end stage (fenced) on block id
+// b, as the page's PullController does, for rank v with its lanes 0..W-1.
+// With tags, thread 0 writes the block's tag between the two stages and
+// thread p < W reads rank p's tag after the end stage (fresh slots per
+// round, as in the pad barrier's check). Returns false on a timeout.
+__device__ __forceinline__ bool counter_round(const CounterArgs& a, int v, uint32_t b, int lane, bool active,
+                                              int r) {
+  const int W = a.world;
+  const size_t nb = (size_t)a.nblocks;
+  // start stage: no fence, workgroup barrier after
+  bool ok = !active || counter_sync(a.sem, W, b, v, lane, false, true, a.split != 0, a.timeout);
+  if (__syncthreads_or(!ok)) return false;
+  if (a.tags && lane == 0 && active) a.tags[((size_t)v * a.rounds + r) * nb + b] = barrier_tag(v, b, r);
+  // end stage: workgroup barrier before, fenced
+  __syncthreads();
+  ok = !active || counter_sync(a.sem, W, b, v, lane, true, false, a.split != 0, a.timeout);
+  if (__syncthreads_or(!ok)) return false;
+  if (a.tag_seen && active && lane < W)
+    a.tag_seen[(((size_t)v * a.rounds + r) * nb + b) * W + lane] = a.tags[((size_t)lane * a.rounds + r) * nb + b];
+  return true;
+}
+
+// One workgroup per rank and block (the default launch), placed as in
+// barrier_groups_kernel. The workgroup reads its rank's epoch for the block
+// first, runs `rounds` rounds, then flips the epoch as PushController's exit
+// does.
+__global__ __launch_bounds__(64) void counter_groups_kernel(CounterArgs a) {
+  const int W = a.world;
+  const int v = (int)(blockIdx.x % (uint32_t)W);
+  const uint32_t b = blockIdx.x / (uint32_t)W;
+  uint32_t* const epochs = select_epochs(a.epochs, v);
+  if (threadIdx.x == 0 && a.seen) a.seen[(size_t)v * a.nblocks + b] = block_epoch(epochs, b);
+  for (int r = 0; r < a.rounds; ++r) {
+    if (!counter_round(a, v, b, (int)threadIdx.x, true, r)) {
+      if (threadIdx.x == 0) report_error(a.ctl, ERR_COUNTER_TIMEOUT, (uint64_t)blockIdx.x);
+      return;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) block_epoch_flip(epochs, b);
+}
+
+// Lane groups (the named variant): workgroup b is one wave; lanes
+// [v * W, v * W + W) play virtual rank v, so every add precedes every wait
+// in one instruction stream and no workgroup waits on another.
+__global__ __launch_bounds__(64) void counter_lanes_kernel(CounterArgs a) {
   const int W = a.world;
   const int t = threadIdx.x;
   const int v = t / W, s = t - v * W;
   const bool active = t < W * W;
-  if (threadIdx.x == 0 && a.seen) a.seen[blockIdx.x] = block_epoch(a.epochs, blockIdx.x);
+  const uint32_t b = blockIdx.x;
+  if (a.seen && active && s == 0) a.seen[(size_t)v * a.nblocks + b] = block_epoch(select_epochs(a.epochs, v), b);
   for (int r = 0; r < a.rounds; ++r) {
-    // start stage: no fence, workgroup barrier after
-    bool ok = !active || counter_sync(a.sem, W, blockIdx.x, v, s, false, true, a.timeout);
+    bool ok = !active || counter_sync(a.sem, W, b, v, s, false, true, a.split != 0, a.timeout);
     if (__syncthreads_or(!ok)) {
       if (threadIdx.x == 0) report_error(a.ctl, ERR_COUNTER_TIMEOUT, (uint64_t)blockIdx.x);
       return;
     }
-    // end stage: workgroup barrier before, fenced
     __syncthreads();
-    ok = !active || counter_sync(a.sem, W, blockIdx.x, v, s, true, false, a.timeout);
+    ok = !active || counter_sync(a.sem, W, b, v, s, true, false, a.split != 0, a.timeout);
     if (__syncthreads_or(!ok)) {
       if (threadIdx.x == 0) report_error(a.ctl, ERR_COUNTER_TIMEOUT, (uint64_t)blockIdx.x);
       return;
     }
   }
-  block_epoch_exit(a.epochs, blockIdx.x);
+  __syncthreads();
+  if (active && s == 0) block_epoch_flip(select_epochs(a.epochs, v), b);
 }
 
-hipError_t launch_counter_barrier(const CounterArgs& a, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL(counter_barrier_kernel, dim3(nblocks), dim3(64), 0, s, a);
+hipError_t launch_counter_barrier(const CounterArgs& a, bool lanes, hipStream_t s) {
+  if (lanes) hipLaunchKernelGGL(counter_lanes_kernel, dim3(a.nblocks), dim3(64), 0, s, a);
+  else hipLaunchKernelGGL(counter_groups_kernel, dim3(a.world * a.nblocks), dim3(64), 0, s, a);
   return hipGetLastError();
+}
+
+// Workgroups of barrier_groups_kernel (or counter_groups_kernel) the device
+// holds at once: occupancy per CU, queried once per kernel, times the CU
+// count; 0 if the query fails.
+long long barrier_groups_cap(bool counter, int cus) {
+  static const int per_cu_pad = [] {
+    int o = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, reinterpret_cast<const void*>(barrier_groups_kernel), 64,
+                                                         0) == hipSuccess
+               ? o
+               : 0;
+  }();
+  static const int per_cu_counter = [] {
+    int o = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, reinterpret_cast<const void*>(counter_groups_kernel), 64,
+                                                         0) == hipSuccess
+               ? o
+               : 0;
+  }();
+  return (long long)(counter ? per_cu_counter : per_cu_pad) * cus;
 }
 
 // ---- symmetric-buffer exchange fenced by the pad barrier's patterns --------
@@ -111,9 +205,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
   for (int src = 0; src < W; ++src) rs[src] = make_rsrc(a.symm + (size_t)src * a.stride, slot_bytes(a.stride));
   const bool tail_block = b == a.blocks - 1;
   // pattern 0
-  bool ok = (int)threadIdx.x >= W ||
-            barrier_signal_wait(select_pad(a.pad, threadIdx.x) + (size_t)b * W + v,
-                                select_pad(a.pad, v) + (size_t)b * W + threadIdx.x, false, a.timeout);
+  bool ok = arx_detail::barrier_lane(a.pad, W, v, b, (int)threadIdx.x, false, a.timeout);
   if (__syncthreads_or(!ok)) goto fail;
   for (int k = 0; k < a.iters; ++k) {
     const uint16_t* in = a.inputs + ((size_t)k * W + v) * a.ld;
@@ -122,9 +214,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
     if (tail_block && threadIdx.x < tail) mine[8u * (size_t)nv + threadIdx.x] = in[8u * (size_t)nv + threadIdx.x];
     // pattern 1
     __syncthreads();
-    ok = (int)threadIdx.x >= W ||
-         barrier_signal_wait(select_pad(a.pad, threadIdx.x) + (size_t)b * W + v,
-                             select_pad(a.pad, v) + (size_t)b * W + threadIdx.x, true, a.timeout);
+    ok = arx_detail::barrier_lane(a.pad, W, v, b, (int)threadIdx.x, true, a.timeout);
     if (__syncthreads_or(!ok)) goto fail;
     for (uint32_t x = lo + threadIdx.x; x < hi; x += kBlock) {
       u32x4 y[W];
@@ -141,9 +231,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
     }
     // pattern 2
     __syncthreads();
-    ok = (int)threadIdx.x >= W ||
-         barrier_signal_wait(select_pad(a.pad, threadIdx.x) + (size_t)b * W + v,
-                             select_pad(a.pad, v) + (size_t)b * W + threadIdx.x, false, a.timeout);
+    ok = arx_detail::barrier_lane(a.pad, W, v, b, (int)threadIdx.x, false, a.timeout);
     if (__syncthreads_or(!ok)) goto fail;
   }
   return;

@@ -1,6 +1,7 @@
-"""The C ABI library loads and exports exactly what include/arx.h declares,
-and its host-side argument checks work without a GPU (CPU only: none of
-these calls reaches the device)."""
+"""The C ABI library loads and exports exactly what include/arx.h and
+include/arx_test.h declare, the public device header compiles on its own in
+a caller's code, and the library's host-side argument checks work without a
+GPU (CPU only: none of these calls reaches the device)."""
 import ctypes
 import os
 import re
@@ -9,14 +10,18 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "arx.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("arx.h", "arx_test.h")]
+DEVICE_HEADER = os.path.join(ROOT, "include", "arx_device.h")
+DEVAPI_LIB = os.path.join(ROOT, "tests", "devapi", "libdevapi_user.so")
 LIB = os.path.join(ROOT, "signal_pad_sync_amd", "libarx.so")
 
 
-def declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(arx_\w+)\s*\(", src, flags=re.M)))
+def declared(headers=HEADERS):
+    names = set()
+    for h in headers:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(arx_\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def exported():
@@ -25,10 +30,45 @@ def exported():
 
 
 def test_header_declares_the_boundary():
-    names = declared()
+    names = declared(HEADERS[:1])
     for must in ("arx_init", "arx_publish", "arx_allreduce", "arx_barrier_blockwise", "arx_reduce"):
         assert must in names
     assert len(names) >= 15
+    aids = declared(HEADERS[1:])
+    assert aids == ["arx_debug_fail_proxy", "arx_debug_set_seq", "arx_debug_state", "arx_test_round_bf16"]
+    assert not set(aids) & set(names)
+
+
+def test_device_header_declares_the_barrier():
+    """include/arx_device.h: arx_pad_t {ptr[8], rank, W, sem, timeout} and
+    barrier_blockwise(arx_pad_t, uint32_t block_id), header-only."""
+    src = open(DEVICE_HEADER).read()
+    assert re.search(r"typedef struct arx_pad \{[^}]*uint32_t\* ptr\[8\];[^}]*int rank;[^}]*int W;[^}]*int sem;"
+                     r"[^}]*uint64_t timeout;[^}]*\} arx_pad_t;", src, flags=re.S)
+    assert re.search(r"__device__ __forceinline__ bool barrier_blockwise\(arx_pad_t pad, uint32_t block_id\)", src)
+
+
+def test_device_header_builds_alone(tmp_path):
+    """A caller's kernel that includes arx_device.h and nothing else of the
+    library compiles for gfx950 (device code only, no GPU needed)."""
+    src = tmp_path / "user.hip"
+    src.write_text('#include "arx_device.h"\n'
+                   '__global__ void k(arx_pad_t p, int* ok) { ok[threadIdx.x] = barrier_blockwise(p, blockIdx.x); }\n')
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "--cuda-device-only", "-c", "-O3",
+                        "-I", os.path.join(ROOT, "include"), str(src), "-o", str(tmp_path / "user.o")],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+
+
+def test_devapi_test_library_uses_only_the_public_header():
+    """The test library of the public device barrier includes arx_device.h
+    and no private header, and exports its one entry point."""
+    src = open(os.path.join(ROOT, "tests", "devapi", "devapi_user.hip")).read()
+    assert re.findall(r'#include "([^"]+)"', src) == ["arx_device.h"]
+    assert os.path.exists(DEVAPI_LIB), "build it first (__graft_entry__.build())"
+    out = subprocess.run(["nm", "-D", "--defined-only", DEVAPI_LIB], check=True, capture_output=True,
+                         text=True).stdout
+    assert "devapi_barrier" in out
 
 
 def test_library_exports_every_declared_symbol_and_no_other():
@@ -59,7 +99,10 @@ def test_host_checks_before_init(L):
     assert L.arx_publish(1) == arx.ESTATE
     assert L.arx_allreduce(None, None, 0, None) == arx.ESTATE
     assert L.arx_reduce(None, None, 0, 0, None) == arx.ESTATE
-    assert L.arx_barrier_blockwise(1, 1, 1, None) == arx.ESTATE
+    assert L.arx_barrier_blockwise(1, 1, 1, 0, None, None, None) == arx.ESTATE
+    assert L.arx_counter_barrier(1, 1, 0, None, None, None, None) == arx.ESTATE
+    assert L.arx_barrier_max_blocks() == arx.ESTATE
+    assert L.arx_epoch_ptr(0) is None and L.arx_sem_ptr(0) is None
     assert L.arx_set_proxy_mode(0) == arx.ESTATE
     assert L.arx_set_timeout_us(10) == arx.ESTATE
     assert L.arx_finalize() == arx.ESTATE

@@ -38,6 +38,7 @@ def test_json_line_fields():
     assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
     assert rf["achieved"] == line["value"] and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-5
     assert rf["bytes_per_launch"] == bytes_call
+    assert rf["event_us_per_launch"] == 9.0 and "kernel_us" not in rf   # event time per launch, named as such
     assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] >= 1
 
 

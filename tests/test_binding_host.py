@@ -63,8 +63,11 @@ def test_calls_check_before_the_library():
         arx.reduce(FakeTensor(10), FakeTensor(1000), 0, 1000, stream=0)
     assert e.value.code == arx.EINVAL
     with pytest.raises(arx.ArxError) as e:
-        arx.counter_barrier(16, 1, FakeTensor(16, itemsize=2), stream=0)
+        arx.counter_barrier(16, 1, epochs_seen=FakeTensor(16, itemsize=2), stream=0)
     assert e.value.code == arx.EINVAL
+    with pytest.raises(arx.ArxError) as e:
+        arx.barrier_blockwise(16, arx.SEM_ACQ_REL, 1, tags=FakeTensor(64, itemsize=4), stream=0)
+    assert e.value.code == arx.EINVAL and "go together" in str(e.value)
     with pytest.raises(arx.ArxError) as e:        # extents fine: the library itself refuses
         arx.allreduce(FakeTensor(1000), FakeTensor(1000), 1000, stream=0)
     assert e.value.code == arx.ESTATE

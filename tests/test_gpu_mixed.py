@@ -36,6 +36,7 @@ def test_mixed_call_sequence(W, rank, seed):
     recv = [[WL.uniform(41000 + 100 * seed + 10 * par + s, max_n) for s in range(W)] for par in (0, 1)]
     rounds_done = np.zeros(arx.MAX_PAD_BLOCKS, np.int64)
     launches = np.zeros(arx.MAX_PAD_BLOCKS, np.int64)
+    split = None                      # the counter barrier's design, fixed by its first launch
     with library(W, max_n, rank=rank):
         fill_recv(recv, rank)
         st = None
@@ -71,22 +72,30 @@ def test_mixed_call_sequence(W, rank, seed):
                 same(got[:n], R.reduce(parts, n=n) if n else got[:0], f"step {step} reduce n={n} par={par}")
                 assert np.all(got[n:] == 0xDEAD)
             elif op == "barrier":
-                nblocks = int(rng.integers(1, arx.MAX_PAD_BLOCKS + 1))
+                lanes = bool(rng.integers(2))
+                most = arx.MAX_PAD_BLOCKS if lanes else arx.barrier_max_blocks()
+                nblocks = int(rng.integers(1, most + 1))
                 sem = int(rng.integers(2))
-                arx.barrier_blockwise(nblocks, sem, int(rng.integers(1, 5)))
+                arx.barrier_blockwise(nblocks, sem, int(rng.integers(1, 5)), arx.BARRIER_LANES if lanes else 0)
                 torch.cuda.synchronize()
             elif op == "counter":
-                nblocks = int(rng.integers(1, arx.MAX_PAD_BLOCKS + 1))
+                lanes = bool(rng.integers(2))
+                if split is None:
+                    split = bool(rng.integers(2))
+                most = arx.MAX_PAD_BLOCKS if lanes else arx.barrier_max_blocks()
+                nblocks = int(rng.integers(1, most + 1))
                 rounds = int(rng.integers(0, 4))
-                arx.counter_barrier(nblocks, rounds)
+                arx.counter_barrier(nblocks, rounds, (arx.BARRIER_LANES if lanes else 0) |
+                                    (arx.BARRIER_SPLIT if split else 0))
                 torch.cuda.synchronize()
                 rounds_done[:nblocks] += rounds
                 launches[:nblocks] += 1
+                per = W if split else 2 * W
                 for r in range(W):
                     sem_r = arx.sem_view(r).cpu().numpy()
-                    assert np.array_equal(sem_r[:, 0], 2 * W * rounds_done), f"step {step}: flags of rank {r}"
-                    assert np.array_equal(sem_r[:, 1], 2 * W * rounds_done), f"step {step}: bases of rank {r}"
-                assert np.array_equal(arx.epoch_view().cpu().numpy(), launches % 2)
+                    assert np.array_equal(sem_r[:, 0], per * rounds_done), f"step {step}: flags of rank {r}"
+                    assert np.array_equal(sem_r[:, 1], per * rounds_done), f"step {step}: bases of rank {r}"
+                    assert np.array_equal(arx.epoch_view(r).cpu().numpy(), launches % 2)
             else:
                 iters = int(rng.integers(1, 4))
                 ld = max(8, (n + 7) & ~7)

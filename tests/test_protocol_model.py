@@ -75,6 +75,32 @@ def test_barrier_mutants_are_caught():
     assert not b2.ok and "not zero" in b2.violation       # pad left dirty
     assert not P.check_barrier(3, 2, mutant="B1").ok
     assert not P.check_barrier(3, 2, mutant="B2").ok
+    b3 = P.check_barrier(2, 2, mutant="B3")                # tags read before consuming
+    assert not b3.ok and "before rank" in b3.violation and "wrote it" in b3.violation
+    assert not P.check_barrier(3, 2, mutant="B3").ok
+
+
+def test_barrier_tag_format():
+    """Tags as the library documents them: 0x80000000 | round << 16 |
+    block << 4 | rank, worked by hand."""
+    assert P.barrier_tag(0, 0, 0) == 0x80000000
+    assert P.barrier_tag(3, 5, 2) == 0x80020053
+    assert P.barrier_tag(7, 1023, 63) == 0x803F3FF7
+    assert P.barrier_tag(1, 16, 1) == 0x80010101
+
+
+def test_barrier_tags_seen_prediction():
+    """After round r every rank's block b sees rank p's round-r tag for block
+    b, whoever reads it; the tag rows hold each rank's own tags."""
+    W, nb, R = 3, 4, 2
+    written = P.barrier_tags_written(W, nb, R)
+    seen = P.barrier_tags_seen(W, nb, R)
+    assert written.shape == (W, R, nb) and seen.shape == (W, R, nb, W)
+    assert written[2, 1, 3] == 0x80010032
+    for v in range(W):
+        for r in range(R):
+            for b in range(nb):
+                assert [int(x) for x in seen[v, r, b]] == [P.barrier_tag(p, b, r) for p in range(W)]
 
 
 def _recv(cfg, W, n):
