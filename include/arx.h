@@ -58,6 +58,7 @@ extern "C" {
 #define ARX_MAX_WORLD 8          /* page "arx.cu": kMaxWorld; page "common.cuh": kMaxNumGPU */
 #define ARX_MAX_PAD_BLOCKS 1024  /* workgroups per barrier launch */
 #define ARX_MAX_N ((size_t)1 << 30) /* elements per partial */
+#define ARX_NOALLOC_MAX_N ((size_t)1 << 20) /* elements per partial of arx_symm_allreduce_noalloc */
 
 /* Proxy modes: when the virtual peers post the flag of seq s. */
 #define ARX_PROXY_LOCKSTEP 0 /* once this rank has published s (peers exactly as fast) */
@@ -244,6 +245,30 @@ int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, i
  * occupancy query failed). The lane-group variant accepts
  * ARX_MAX_PAD_BLOCKS. Errors: ARX_ESTATE. */
 int arx_barrier_max_blocks(void);
+
+/*
+ * arx_symm_allreduce_noalloc — arx_symm_allreduce for callers that cannot
+ * allocate device memory: code under hipGraph capture, tight serving loops,
+ * harnesses that forbid allocation. Same kernel, same results, but needs no
+ * arx_init and allocates nothing: the W symmetric buffers and the signal
+ * pads live in one fixed array in device memory that the library's code
+ * object holds on every GPU it is loaded on, until the process ends
+ * (ARX_MAX_WORLD x ARX_NOALLOC_MAX_N bf16 plus 16 KiB of pads: about
+ * 16 MiB per GPU). Each call first zero-fills the pads it uses (one small
+ * kernel; a completed exchange leaves them zero, one that timed out may
+ * not), then runs the exchange, both on `stream`.
+ *   world: W in [2, 8].  inputs, outputs, ld, iters: as arx_symm_allreduce.
+ *   n <= ARX_NOALLOC_MAX_N.  status: device u32, 4-byte aligned, or NULL;
+ *   set to 1 if a barrier wait timed out (2 s), when that call's outputs are
+ *   incomplete; never cleared by the library.
+ * Every call on one GPU uses the same array, which keeps the last call's
+ * contents: calls that overlap on one GPU (concurrent streams, threads)
+ * race and must be ordered by the caller.
+ * Errors (nothing launched): ARX_EINVAL (arguments, n beyond the limit),
+ * ARX_EHIP.
+ */
+int arx_symm_allreduce_noalloc(int world, const void* inputs, void* outputs, size_t n, size_t ld, int iters,
+                               uint32_t* status, hipStream_t stream);
 
 /* Device address of rank `rank`'s semaphores: ARX_MAX_PAD_BLOCKS entries of
  * 32 u32 (128 bytes): flag at [0] and base at [1], the split design's

@@ -17,6 +17,7 @@ PROXY_LOCKSTEP, PROXY_RUNAHEAD, PROXY_MANUAL, PROXY_STRESS = 0, 1, 2, 3
 SEM_RELAXED, SEM_ACQ_REL = 0, 1
 BARRIER_LANES, BARRIER_SPLIT = 1, 2
 MAX_WORLD, MAX_PAD_BLOCKS, MAX_N = 8, 1024, 1 << 30
+NOALLOC_MAX_N = 1 << 20
 
 # names of arx_debug_state's words, in order
 STATE_WORDS = ["seq_dev", "cnt0", "cnt1", "go", "abort", "ctl_seq", "ctl_bytes0", "ctl_bytes1",
@@ -38,6 +39,8 @@ SIGNATURES = [
     ("arx_counter_barrier", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                        _c.c_void_p]),
     ("arx_symm_allreduce", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_size_t, _c.c_int, _c.c_void_p]),
+    ("arx_symm_allreduce_noalloc", _c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_size_t, _c.c_int,
+                                              _c.c_void_p, _c.c_void_p]),
     ("arx_barrier_max_blocks", _c.c_int, []),
     ("arx_sem_ptr", _c.c_void_p, [_c.c_int]),
     ("arx_epoch_ptr", _c.c_void_p, [_c.c_int]),
@@ -178,6 +181,19 @@ def counter_barrier(nblocks: int, rounds: int = 1, flags: int = 0, epochs_seen=N
     ptr = None if epochs_seen is None else _buf(epochs_seen, world() * nblocks, "epochs_seen", 4)
     tp, sp = _tag_bufs(tags, seen, rounds, nblocks)
     _check(lib.arx_counter_barrier(nblocks, rounds, flags, ptr, tp, sp, _stream(stream)))
+
+
+def symm_allreduce_noalloc(world_size: int, inputs, outputs, n: int, iters: int, status=None, stream=None):
+    """The symmetric exchange with no allocation and no library instance:
+    inputs / outputs bf16 device tensors [iters, W, ld]; status: optional
+    int32 device tensor of one element, set to 1 on a timeout."""
+    ld = inputs.shape[-1]
+    if tuple(outputs.shape[-1:]) != (ld,):
+        raise ArxError(EINVAL, "inputs and outputs must have the same last dimension")
+    need = iters * world_size * ld
+    sp = None if status is None else _buf(status, 1, "status", 4)
+    _check(lib.arx_symm_allreduce_noalloc(world_size, _buf(inputs, need, "inputs"), _buf(outputs, need, "outputs"),
+                                          n, ld, iters, sp, _stream(stream)))
 
 
 def barrier_max_blocks() -> int:

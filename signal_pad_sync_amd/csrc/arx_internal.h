@@ -111,7 +111,8 @@ struct SymmArgs {
   int world;
   uint32_t* pad[8];
   uint64_t timeout;
-  Ctl* ctl;
+  Ctl* ctl;                // pinned control block for a timeout report, or null
+  uint32_t* status;        // device word set to 1 on a timeout, or null
 };
 
 // Launchers (defined in arx_reduce.hip and arx_sync.hip). W in [2, 8]. block: threads per
@@ -131,6 +132,10 @@ long long barrier_groups_cap(bool counter, int cus);
 hipError_t launch_symm_allreduce(const SymmArgs& a, hipStream_t stream);
 int symm_blocks(uint32_t n, int world, int cus);
 hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStream_t stream);
+
+// Records the detail of an error for arx_strerror and returns `code`
+// (defined in arx_runtime.cpp).
+int set_error(int code, const char* fmt, ...);
 
 // Grid the one-shot kernel uses for n elements with `block` threads per
 // workgroup, at most max_grid (all its workgroups must be resident at once,

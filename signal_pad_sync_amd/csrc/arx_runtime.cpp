@@ -252,6 +252,16 @@ int check_groups(int nblocks, bool counter) {
 
 }  // namespace
 
+namespace arx {
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return code;
+}
+}  // namespace arx
+
 extern "C" {
 
 int arx_init(int world, size_t max_n) { return init_impl(world, max_n, 0); }
@@ -401,6 +411,7 @@ int arx_symm_allreduce(const void* inputs, void* outputs, size_t n, size_t ld, i
     a.pad[i] = i < S.world ? S.pads + (size_t)i * ARX_MAX_PAD_BLOCKS * S.world : nullptr;
   a.timeout = timeout_ticks();
   a.ctl = S.ctl_dev;
+  a.status = nullptr;
   HIPCHK(arx::launch_symm_allreduce(a, stream));
   return ARX_OK;
 }

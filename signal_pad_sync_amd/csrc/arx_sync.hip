@@ -11,6 +11,9 @@
 //                            by the pad barrier's usage patterns
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+#include "arx.h"
 #include "arx_prims.h"
 #include "arx_internal.h"
 #include "arx_kernel_util.h"
@@ -236,7 +239,10 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
   }
   return;
 fail:
-  if (threadIdx.x == 0) report_error(a.ctl, ERR_SYMM_TIMEOUT, (uint64_t)blockIdx.x);
+  if (threadIdx.x == 0) {
+    if (a.ctl) report_error(a.ctl, ERR_SYMM_TIMEOUT, (uint64_t)blockIdx.x);
+    if (a.status) store_relaxed_system(a.status, 1u);
+  }
 }
 
 // Workgroups per rank, G: aim for about 128 workgroups in all (W * G),
@@ -303,4 +309,108 @@ hipError_t launch_symm_allreduce(const SymmArgs& a, hipStream_t s) {
   }
 }
 
+// ---- the symmetric exchange with no allocation -----------------------------
+
+// For callers that cannot allocate (code under hipGraph capture, tight
+// serving loops, harnesses that forbid allocation): the symmetric buffers
+// and signal pads of the exchange live in this fixed array, which the
+// library's code object holds on every GPU it is loaded on until the process
+// ends. Layout: W symmetric buffers of kNoAllocMaxN bf16 (rank v's at
+// v * kNoAllocMaxN elements), then the pads, rank r's u32 [kSymmMaxBlocks][W]
+// at r * kSymmMaxBlocks * W words after the buffers.
+constexpr size_t kNoAllocMaxN = ARX_NOALLOC_MAX_N;
+constexpr size_t kSymmMaxBlocks = 64;
+constexpr size_t kScratchBufBytes = (size_t)ARX_MAX_WORLD * kNoAllocMaxN * sizeof(uint16_t);
+constexpr size_t kScratchPadWords = (size_t)ARX_MAX_WORLD * kSymmMaxBlocks * ARX_MAX_WORLD;
+constexpr size_t kScratchBytes = kScratchBufBytes + kScratchPadWords * sizeof(uint32_t);
+static_assert(kNoAllocMaxN % 128 == 0, "symmetric buffers start on 256-byte boundaries");
+
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
+
+// Zero-fills the pads of one exchange before it runs: a completed exchange
+// leaves them zero, one that timed out may not.
+__global__ __launch_bounds__(kBlock) void clear_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = threadIdx.x; i < n; i += kBlock) p[i] = 0u;
+}
+
+namespace {
+
+// Per device: the array's device address (hipGetSymbolAddress, taken with
+// that device current), its CU count and its wall-clock rate.
+struct ScratchDev {
+  void* ptr = nullptr;
+  int cus = 0;
+  uint64_t khz = 0;
+};
+constexpr int kMaxDevices = 64;
+ScratchDev g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_for_device(ScratchDev* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(ARX_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(ARX_EINVAL, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  ScratchDev& d = g_scratch[dev];
+  if (!d.ptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return set_error(ARX_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    int cus = 0, khz = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess ||
+        (e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+      return set_error(ARX_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    d.cus = cus;
+    d.khz = khz > 0 ? (uint64_t)khz : 100000u;
+    d.ptr = p;
+  }
+  *out = d;
+  return ARX_OK;
+}
+
+}  // namespace
+
 }  // namespace arx
+
+extern "C" int arx_symm_allreduce_noalloc(int world, const void* inputs, void* outputs, size_t n, size_t ld,
+                                          int iters, uint32_t* status, hipStream_t stream) {
+  using namespace arx;
+  if (world < 2 || world > ARX_MAX_WORLD) return set_error(ARX_EINVAL, "world %d not in [2, %d]", world, ARX_MAX_WORLD);
+  if (n > kNoAllocMaxN) return set_error(ARX_EINVAL, "n %zu exceeds ARX_NOALLOC_MAX_N %zu", n, kNoAllocMaxN);
+  if (ld < n || (ld & 7u)) return set_error(ARX_EINVAL, "ld %zu must be >= n and a multiple of 8", ld);
+  if (iters < 1 || iters > 65536) return set_error(ARX_EINVAL, "iters %d not in [1, 65536]", iters);
+  if (n > 0 && (inputs == nullptr || outputs == nullptr)) return set_error(ARX_EINVAL, "null inputs or outputs");
+  if (((uintptr_t)inputs & 15u) || ((uintptr_t)outputs & 15u) || ((uintptr_t)status & 3u))
+    return set_error(ARX_EINVAL, "inputs and outputs must be 16-byte aligned, status 4-byte aligned");
+  const size_t extent = (size_t)iters * world * ld * sizeof(uint16_t);
+  const uintptr_t x = (uintptr_t)inputs, y = (uintptr_t)outputs;
+  if (inputs != outputs && n > 0 && x < y + extent && y < x + extent)
+    return set_error(ARX_EINVAL, "inputs and outputs overlap without being the same buffer");
+  ScratchDev d;
+  int rc = scratch_for_device(&d);
+  if (rc != ARX_OK) return rc;
+  SymmArgs a;
+  a.inputs = (const uint16_t*)inputs;
+  a.outputs = (uint16_t*)outputs;
+  a.symm = (uint16_t*)d.ptr;
+  a.stride = kNoAllocMaxN;
+  a.ld = ld;
+  a.n = (uint32_t)n;
+  a.iters = iters;
+  a.world = world;
+  a.blocks = symm_blocks(a.n, world, d.cus);
+  if (a.blocks < 1 || (size_t)a.blocks > kSymmMaxBlocks)
+    return set_error(ARX_EHIP, "no workgroup count for the exchange (occupancy query failed?)");
+  uint32_t* const pads = reinterpret_cast<uint32_t*>(static_cast<char*>(d.ptr) + kScratchBufBytes);
+  for (int i = 0; i < 8; ++i) a.pad[i] = i < world ? pads + (size_t)i * kSymmMaxBlocks * world : nullptr;
+  a.timeout = 2000000ull * d.khz / 1000u;   // 2 s
+  a.ctl = nullptr;
+  a.status = status;
+  hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(kBlock), 0, stream, pads,
+                     (uint32_t)((size_t)world * kSymmMaxBlocks * world));
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = launch_symm_allreduce(a, stream);
+  if (e != hipSuccess) return set_error(ARX_EHIP, "launching the exchange: %s", hipGetErrorString(e));
+  return ARX_OK;
+}

@@ -128,3 +128,19 @@ def test_strerror_codes(L):
     for code in range(-7, 1):
         assert L.arx_strerror(code)
     assert L.arx_strerror(-99) == b"unknown error"
+
+
+def test_noalloc_argument_checks_need_no_gpu(L):
+    """arx_symm_allreduce_noalloc refuses bad arguments before any HIP call:
+    world, n beyond ARX_NOALLOC_MAX_N, ld, iters, alignment, overlap."""
+    from signal_pad_sync_amd import arx
+    big = arx.NOALLOC_MAX_N
+    base = 1 << 20
+    for args in [(1, base, base + 4096, 8, 8, 1, None), (9, base, base + 4096, 8, 8, 1, None),
+                 (2, base, base + (1 << 24), big + 1, big + 8, 1, None),
+                 (2, base, base + 4096, 16, 8, 1, None), (2, base, base + 4096, 9, 12, 1, None),
+                 (2, base, base + 4096, 8, 8, 0, None), (2, base, base + 4096, 8, 8, 65537, None),
+                 (2, None, base, 8, 8, 1, None), (2, base + 8, base + 4096, 8, 8, 1, None),
+                 (2, base, base + 4096, 8, 8, 1, base + 8192 + 2),
+                 (2, base, base + 16, 8, 8, 1, None)]:
+        assert L.arx_symm_allreduce_noalloc(*args, None) == arx.EINVAL, args
