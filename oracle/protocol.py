@@ -158,6 +158,8 @@ MUTANTS = {
     "M4": "one counter shared by the arrival and the finish phase",
     "M5": "workgroups other than 0 do not wait for go",
     "M6": "the arrival count publishes one copying workgroup early",
+    "M7": "with early_finish, workgroup 0 also counts itself finished before its flag wait",
+    "M8": "with early_finish, a workgroup other than 0 counts itself finished before it reads the seq",
 }
 
 
@@ -174,7 +176,8 @@ class CheckResult:
 
 
 def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
-                   max_states: int = 5_000_000, copiers: Optional[int] = None) -> CheckResult:
+                   max_states: int = 5_000_000, copiers: Optional[int] = None,
+                   early_finish: bool = False) -> CheckResult:
     """Explores every interleaving of W ranks x G workgroups x S calls.
 
     copiers: the number C of workgroups that copy and count arrival (default
@@ -188,6 +191,18 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
     copied after its reduction: go follows the peers' flags, which do not
     wait for this rank's copies.)
 
+    early_finish: where the last-block-out count comes (page "arx.cu",
+    arx_kernel: the finish counter, the last block out records the finished
+    seq). By default every workgroup counts itself finished after its
+    reduction, as on the page. With early_finish a workgroup other than 0
+    counts itself finished as soon as it has read the seq and passed the
+    arrival step, and workgroup 0 right after its flag wait: the count only
+    has to follow every workgroup's read of seq_dev (the last one to count
+    advances it) and, so that the recorded finished seq means the peers'
+    flags were seen, workgroup 0's flag wait. Checked in every mode: when the
+    last workgroup to count records seq s as finished, workgroup 0 has passed
+    its flag wait for s.
+
     Rank state tuple: (c, pcs, ss, cnt0, cnt1, go, seq_dev, ctl_seq, done,
     send, recv, flag, posted, pcur, ppos) where c is the running call (S + 1
     after the last), pcs/ss the per-workgroup program counter and seq,
@@ -197,6 +212,8 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
     """
     if mutant not in MUTANTS:
         raise ValueError(mutant)
+    if mutant in ("M7", "M8") and not early_finish:
+        raise ValueError(f"{mutant} is a mutant of early_finish")
     C = G if copiers is None else copiers
     if not 1 <= C <= G:
         raise ValueError(f"copiers {C} not in [1, {G}]")
@@ -207,6 +224,32 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
 
     def par_of(s):
         return 0 if mutant == "M2" else s & 1
+
+    def start_pc(g):
+        # M8: a workgroup other than 0 counts itself finished before it reads the seq
+        return LASTOUT if (mutant == "M8" and g != 0) else READSEQ
+
+    def after_seq(g):
+        if g < C:
+            return COPY
+        return LASTOUT if (early_finish and g != 0 and mutant != "M8") else WAIT
+
+    def after_arrive(g):
+        if early_finish and (g != 0 or mutant == "M7") and not (mutant == "M8" and g != 0):
+            return LASTOUT
+        return WAIT
+
+    def after_lastout(g):
+        if not early_finish:
+            return DONE
+        if g == 0:
+            return WAIT if mutant == "M7" else REDUCE
+        return READSEQ if mutant == "M8" else WAIT
+
+    def wg0_past_wait(pc0):
+        if pc0 in (REDUCE, DONE):
+            return True
+        return pc0 == LASTOUT and mutant != "M7"   # otherwise workgroup 0 counts after its flag wait
 
     # Proxy actions for one seq, staggered peer order r+1, r+2, ... (page
     # "arx.cu": each rank sends to the next ranks in turn). Data first, then
@@ -222,7 +265,7 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
 
     acts = [actions(r) for r in range(W)]
 
-    init_rank = (1, (READSEQ,) * G, (0,) * G, 0, 0, 0, 0, 0, 0,
+    init_rank = (1, tuple(start_pc(g) for g in range(G)), (0,) * G, 0, 0, 0, 0, 0, 0,
                  (0,) * (2 * G), (0,) * (2 * W * G), (0,) * W, 0, 0, 0)
     init = tuple(init_rank for _ in range(W))
 
@@ -247,7 +290,7 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                     ns = None
                     if pc == READSEQ:
                         s2 = seq_dev + 1
-                        nxt = COPY if g < C else WAIT
+                        nxt = after_seq(g)
                         ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss[:g] + (s2,) + ss[g + 1:],
                               cnt0, cnt1, go, seq_dev, ctl_seq, done, send, recv, flag, posted, pcur, ppos)
                     elif pc == COPY:
@@ -264,16 +307,18 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                         if old == last_arrival:   # last copier publishes and resets
                             n0 = 0
                             cs = s
+                        nxt = after_arrive(g)
                         if mutant == "M4":    # one counter for both phases
-                            ns = (c, pcs[:g] + (WAIT,) + pcs[g + 1:], ss, n0, n0, go, seq_dev, cs,
+                            ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss, n0, n0, go, seq_dev, cs,
                                   done, send, recv, flag, posted, pcur, ppos)
                         else:
-                            ns = (c, pcs[:g] + (WAIT,) + pcs[g + 1:], ss, n0, cnt1, go, seq_dev, cs,
+                            ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss, n0, cnt1, go, seq_dev, cs,
                                   done, send, recv, flag, posted, pcur, ppos)
                     elif pc == WAIT:
                         if g == 0:
                             if all(flag[j] >= s for j in range(W) if j != r):
-                                ns = (c, pcs[:g] + (REDUCE,) + pcs[g + 1:], ss, cnt0, cnt1, s, seq_dev,
+                                nxt = LASTOUT if (early_finish and mutant != "M7") else REDUCE
+                                ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss, cnt0, cnt1, s, seq_dev,
                                       ctl_seq, done, send, recv, flag, posted, pcur, ppos)
                         elif mutant == "M5" or go >= s:
                             ns = (c, pcs[:g] + (REDUCE,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
@@ -288,7 +333,8 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                                 return CheckResult(False, len(seen), (
                                     f"rank {r} wg {g} reduced seq {s} with stale data from rank {j} "
                                     f"(tag {t // 64},{t % 64})"))
-                        ns = (c, pcs[:g] + (LASTOUT,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
+                        nxt = DONE if early_finish else LASTOUT
+                        ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
                               ctl_seq, done, send, recv, flag, posted, pcur, ppos)
                     elif pc == LASTOUT:
                         base = cnt0 if mutant == "M4" else cnt1
@@ -296,23 +342,25 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                         sd, dn = seq_dev, done
                         if base == G - 1:     # last block out
                             n1 = 0
-                            sd = s
-                            dn = s
-                        pcs2 = pcs[:g] + (DONE,) + pcs[g + 1:]
-                        c2 = c
-                        if all(x == DONE for x in pcs2):   # the kernel ends
-                            c2 = c + 1
-                            pcs2 = ((READSEQ,) if c2 <= S else (FIN,)) * G
-                            final_cnt = (n1, n1) if mutant == "M4" else (cnt0, n1)
-                            if final_cnt != (0, 0):
+                            sd = ss[0] if (mutant == "M8" and g != 0) else s
+                            dn = sd
+                            if not wg0_past_wait(pcs[0]) or (g == 0 and mutant == "M7"):
                                 return CheckResult(False, len(seen), (
-                                    f"rank {r} kernel {c} ended with counters {final_cnt}"))
+                                    f"rank {r} recorded seq {sd} finished before workgroup 0 saw its flags"))
                         if mutant == "M4":
-                            ns = (c2, pcs2, ss, n1, n1, go, sd, ctl_seq, dn, send, recv, flag,
-                                  posted, pcur, ppos)
+                            ns = (c, pcs[:g] + (after_lastout(g),) + pcs[g + 1:], ss, n1, n1, go, sd,
+                                  ctl_seq, dn, send, recv, flag, posted, pcur, ppos)
                         else:
-                            ns = (c2, pcs2, ss, cnt0, n1, go, sd, ctl_seq, dn, send, recv, flag,
-                                  posted, pcur, ppos)
+                            ns = (c, pcs[:g] + (after_lastout(g),) + pcs[g + 1:], ss, cnt0, n1, go, sd,
+                                  ctl_seq, dn, send, recv, flag, posted, pcur, ppos)
+                    if ns is not None and all(x == DONE for x in ns[1]):   # the kernel ends
+                        c2 = c + 1
+                        pcs2 = tuple(start_pc(g2) if c2 <= S else FIN for g2 in range(G))
+                        final_cnt = (ns[3], ns[4])
+                        if final_cnt != (0, 0):
+                            return CheckResult(False, len(seen), (
+                                f"rank {r} kernel {c} ended with counters {final_cnt}"))
+                        ns = (c2, pcs2) + ns[2:]
                     if ns is not None:
                         succ.append(replace(st, r, ns))
             # ---- proxy of rank r

@@ -61,6 +61,32 @@ def test_publish_before_the_last_copier_is_caught():
         P.check_protocol(2, 2, 2, copiers=3)
 
 
+@pytest.mark.parametrize("W,G,S,C", [(2, 1, 4, None), (2, 2, 3, None), (3, 1, 3, None), (3, 2, 2, None),
+                                     (4, 1, 2, None), (2, 2, 3, 1), (2, 3, 2, 2), (3, 2, 2, 1)])
+def test_protocol_with_early_finish(W, G, S, C):
+    """The kernel's order: workgroups other than 0 count themselves finished
+    once they have read the seq and passed the arrival step, workgroup 0 once
+    it has seen the flags. Still safe and live, counters zero at every kernel
+    end, and the finished seq is recorded only after workgroup 0's flag wait."""
+    r = P.check_protocol(W, G, S, copiers=C, early_finish=True)
+    assert r.ok, r.violation
+    assert r.finals == 1
+
+
+def test_early_finish_mutants_are_caught():
+    """M7: workgroup 0 counting itself finished before its flag wait records
+    the seq as finished before the flags came. M8: a workgroup counting
+    itself finished before reading the seq can read the next call's seq and
+    reduce stale data (or wedge the protocol)."""
+    for W, G, S, C in [(2, 2, 3, None), (2, 2, 2, 1), (2, 3, 2, 2)]:
+        m7 = P.check_protocol(W, G, S, copiers=C, early_finish=True, mutant="M7")
+        assert not m7.ok and "before workgroup 0 saw its flags" in m7.violation, (W, G, S, C)
+        m8 = P.check_protocol(W, G, S, copiers=C, early_finish=True, mutant="M8")
+        assert not m8.ok, (W, G, S, C)
+    with pytest.raises(ValueError):
+        P.check_protocol(2, 2, 2, mutant="M7")
+
+
 @pytest.mark.parametrize("W,K", [(2, 1), (2, 3), (2, 4), (3, 2), (3, 3)])
 def test_barrier_safe_live_and_zero(W, K):
     r = P.check_barrier(W, K)
