@@ -25,8 +25,11 @@ extern "C" {
  * [2] finish counter, [3] go, [4] abort, [5] ctl.seq, [6] ctl.bytes[0],
  * [7] ctl.bytes[1], [8] ctl.done, [9] ctl.err, [10] ctl.err_seq,
  * [11] posted, [12 .. 12+W) flags[src]. seq_dev, ctl.seq, ctl.done, posted
- * abort and the flags are 64-bit sequence numbers; go holds the low 32 bits
- * of one. Returns the number of words written.
+ * and the flags are 64-bit sequence numbers. [3] and [4] are read from the
+ * device's go word, which holds the seq of the last call that passed its
+ * flag wait and whether that call was aborted: [3] is the low 32 bits of
+ * that seq, [4] the seq if the call was aborted (its flag wait timed out and
+ * it summed nothing), else 0. Returns the number of words written.
  */
 int arx_debug_state(uint64_t* words, int nwords);
 

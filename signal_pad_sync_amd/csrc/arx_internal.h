@@ -41,10 +41,12 @@ enum : int {
   WORD_SEQ = 0,      // last completed seq (u64: words 0 and 1)
   WORD_CNT0 = 64,    // workgroups past the copy (arrival counter)
   WORD_CNT1 = 128,   // workgroups finished (finish counter)
-  WORD_GO = 192,     // seq whose peer data has all arrived
-  WORD_ABORT = 256,  // seq whose wait timed out, its reduction skipped (u64: words 256 and 257)
+  WORD_GO = 192,     // go (u64): 2 * seq of the call whose peer data has all arrived, + 1 if that call
+                     // is aborted; kGoReplicas copies, WORD_GO + 64 * k for replica k
   WORDS_TOTAL = 1024,
 };
+constexpr int kGoReplicas = 8;
+static_assert(WORD_GO + 64 * kGoReplicas <= WORDS_TOTAL, "go replicas fit in the word block");
 
 constexpr int kBlock = 256;       // threads per workgroup of the reduction kernels
 constexpr int kMaxOneShotGrid = 256;  // co-resident workgroups of the one-shot kernel

@@ -41,6 +41,12 @@ __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t byte
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, CP);
 }
 
+// Replica k of the one-shot kernel's go word (WORD_GO, one 256-byte line
+// per replica).
+__device__ __forceinline__ uint64_t* go_word(uint32_t* words, uint32_t k) {
+  return reinterpret_cast<uint64_t*>(words + WORD_GO + 64u * k);
+}
+
 __device__ __forceinline__ uint32_t slot_bytes(uint64_t stride) {
   return (uint32_t)(stride * 2u);
 }

@@ -73,6 +73,12 @@ __device__ __forceinline__ uint32_t fetch_add_relaxed_agent(uint32_t* p, uint32_
 }
 
 __device__ __forceinline__ void fence_acquire_system() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, ""); }
+// Acquire and release in one fence (L2 write-back and invalidate), with the
+// same hard wait as the releases above.
+__device__ __forceinline__ void fence_acq_rel_system() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "");
+  __builtin_amdgcn_s_waitcnt(0);
+}
 __device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Constant-rate clock (the wall clock; its rate is a device attribute).

@@ -35,16 +35,14 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   uint64_t* const seq_dev = reinterpret_cast<uint64_t*>(a.words + WORD_SEQ);
   uint32_t* const cnt0 = a.words + WORD_CNT0;
   uint32_t* const cnt1 = a.words + WORD_CNT1;
-  uint32_t* const go = a.words + WORD_GO;
-  uint64_t* const abort_w = reinterpret_cast<uint64_t*>(a.words + WORD_ABORT);
 
   // seq and parity: one more than the last completed call. seq is 64-bit
-  // like the host's flags; go holds its low 32 bits (compared by signed
-  // difference), abort all 64 (a call's abort must never match the zero the
-  // word starts at, which a low half of 0 at seq 2^32 would).
+  // like the host's flags. The go word holds 2 * seq, plus 1 when the call
+  // is aborted, so one load tells a workgroup both that it may go on and
+  // whether to sum; it is never zero for a call (seq >= 1), the value the
+  // word starts at.
   const uint64_t seq = load_relaxed_agent(seq_dev) + 1u;
-  const uint32_t seq32 = (uint32_t)seq;
-  const uint32_t par = seq32 & 1u;
+  const uint32_t par = (uint32_t)seq & 1u;
   uint16_t* const mine = a.send + (size_t)par * a.stride;
   const uint32_t nv = a.n >> 3, tail = a.n & 7u;
   const uint32_t tid = blockIdx.x * BLOCK + threadIdx.x;
@@ -98,43 +96,49 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   uint32_t finished = 0;
   if (!single && blockIdx.x != 0 && threadIdx.x == 0) finished = fetch_add_relaxed_agent(cnt1, 1u);
 
-  // 3. flag wait and go broadcast (page "arx.cu", protocol comment): W - 1
-  //    lanes of workgroup 0 poll the pinned flags over PCIe until each holds
-  //    seq or more; workgroup 0 then stores seq into the device's go word,
-  //    which is all the other workgroups poll
+  // 3. flag wait, then go (page "arx.cu", protocol comment: only one block
+  //    reads the peers' flags, the others learn of them from device
+  //    memory). In workgroup 0, the lane of each peer rank reads that peer's
+  //    pinned flag over PCIe until it reaches seq. The wave then takes one
+  //    fence that both acquires what the flags publish and releases it
+  //    further, and its first 8 lanes store the go value into 8 replicas of
+  //    the go word, one 256-byte line each; workgroup b polls replica b % 8,
+  //    so the workgroups of each XCD (dealt round robin) share a line and no
+  //    line has more than a few pollers.
   bool abort;
   if (blockIdx.x == 0) {
-    bool ok = true;
-    if ((int)threadIdx.x < W && (int)threadIdx.x != a.rank) {
-      const uint64_t t0 = now_ticks();
-      while (load_relaxed_system(a.flags + threadIdx.x) < seq) {
-        if (now_ticks() - t0 > a.timeout) {
-          ok = false;
-          break;
+    if (threadIdx.x < 64) {
+      bool ok = true;
+      if ((int)threadIdx.x < W && (int)threadIdx.x != a.rank) {
+        const uint64_t t0 = now_ticks();
+        while (load_relaxed_system(a.flags + threadIdx.x) < seq) {
+          if (now_ticks() - t0 > a.timeout) {
+            ok = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(1);
+      }
+      const bool bad = __any(!ok);
+      fence_acq_rel_system();
+      if (threadIdx.x < kGoReplicas) store_relaxed_agent(go_word(a.words, threadIdx.x), (seq << 1) | (bad ? 1u : 0u));
+      if (threadIdx.x == 0) {
+        if (bad) report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
+        if (!single) finished = fetch_add_relaxed_agent(cnt1, 1u);
+        s_abort = bad ? 1u : 0u;
       }
     }
-    // the polling wave acquires; the workgroup barrier orders the others
-    if (threadIdx.x < 64) fence_acquire_system();
-    const int bad = __syncthreads_or(!ok);
-    if (threadIdx.x == 0) {
-      if (bad) {
-        store_relaxed_agent(abort_w, seq);
-        report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
-      }
-      if (single) store_relaxed_agent(go, seq32);   // no other workgroup waits on it
-      else {
-        store_release_agent(go, seq32);
-        finished = fetch_add_relaxed_agent(cnt1, 1u);
-      }
-    }
-    abort = bad != 0;
+    // the other waves of workgroup 0 are ordered after the polling wave's
+    // acquire by the workgroup barrier
+    __syncthreads();
+    abort = s_abort != 0u;
   } else {
     if (threadIdx.x == 0) {
+      const uint64_t* const go = go_word(a.words, blockIdx.x % kGoReplicas);
       const uint64_t t0 = now_ticks();
       bool timed = false;
-      while ((int32_t)(load_relaxed_agent(go) - seq32) < 0) {
+      uint64_t g;
+      while (((g = load_relaxed_agent(go)) >> 1) < seq) {
         if (now_ticks() - t0 > 2u * a.timeout) {
           timed = true;
           break;
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
       }
       fence_acquire_agent();
       if (timed) report_error(a.ctl, ERR_GO_TIMEOUT, seq);
-      s_abort = (timed || load_relaxed_agent(abort_w) == seq) ? 1u : 0u;
+      s_abort = (timed || (g & 1u) != 0u) ? 1u : 0u;
     }
     __syncthreads();
     abort = s_abort != 0u;

@@ -500,8 +500,10 @@ int arx_debug_state(uint64_t* words, int nwords) {
   all[0] = dw[arx::WORD_SEQ] | (uint64_t)dw[arx::WORD_SEQ + 1] << 32;
   all[1] = dw[arx::WORD_CNT0];
   all[2] = dw[arx::WORD_CNT1];
-  all[3] = dw[arx::WORD_GO];
-  all[4] = dw[arx::WORD_ABORT] | (uint64_t)dw[arx::WORD_ABORT + 1] << 32;
+  // go (replica 0): 2 * seq of the last call past its flag wait, + 1 if aborted
+  const uint64_t go = dw[arx::WORD_GO] | (uint64_t)dw[arx::WORD_GO + 1] << 32;
+  all[3] = (go >> 1) & 0xFFFFFFFFull;
+  all[4] = (go & 1u) ? go >> 1 : 0u;
   all[5] = load_acquire(&S.ctl->seq);
   all[6] = load_acquire(&S.ctl->bytes[0]);
   all[7] = load_acquire(&S.ctl->bytes[1]);
@@ -522,9 +524,10 @@ int arx_debug_set_seq(uint64_t seq) {
   if (mode != ARX_PROXY_LOCKSTEP && mode != ARX_PROXY_MANUAL)
     return fail(ARX_ESTATE, "set the seq in lockstep or manual mode");
   HIPCHK(hipDeviceSynchronize());
-  uint32_t w[2] = {(uint32_t)seq, (uint32_t)(seq >> 32)};
-  HIPCHK(hipMemcpy(S.words + arx::WORD_SEQ, w, sizeof w, hipMemcpyHostToDevice));
-  HIPCHK(hipMemcpy(S.words + arx::WORD_GO, w, sizeof(uint32_t), hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(S.words + arx::WORD_SEQ, &seq, sizeof seq, hipMemcpyHostToDevice));
+  const uint64_t go = seq << 1;
+  for (int k = 0; k < arx::kGoReplicas; ++k)
+    HIPCHK(hipMemcpy(S.words + arx::WORD_GO + 64 * k, &go, sizeof go, hipMemcpyHostToDevice));
   store_release(&S.ctl->done, seq);
   store_release(&S.ctl->seq, seq);
   S.core->reset(seq);
