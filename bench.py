@@ -66,7 +66,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only", default="", help="comma list of phases: copy,oneshot,runahead,floor,graph,reduce,barrier,symm; "
-                    "configs (every workload, oracle included) runs only when named")
+                    "copy1g (a 1 GiB copy, for the byte counters) and configs (every workload, oracle "
+                    "included) run only when named")
     return ap.parse_args()
 
 
@@ -248,20 +249,25 @@ def bench_barrier(args, kind):
     return us / (reps * per)
 
 
-def bench_copy(args):
-    """A plain device-to-device copy of 64 MiB: the known-size kernel that
-    scales the HBM byte counters. Its rate is not an HBM ceiling: 64 MiB
-    fits in the 256 MB last-level cache (MALL); a copy of 512 MiB reaches
-    about 4.9 TB/s."""
+def bench_copy(args, mib=64):
+    """A plain device-to-device copy of `mib` MiB: the known-size kernel that
+    scales the HBM byte counters. At 64 MiB source and destination fit in
+    the 256 MB last-level cache (MALL), so its rate is not an HBM ceiling;
+    at 1 GiB they do not, and the copy streams through HBM."""
     import torch
-    n = 32 << 20
-    a = torch.randn(n, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    n = mib << 19   # bf16 elements
+    if mib <= 64:
+        a = torch.randn(n, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    else:
+        a = torch.empty(n, device="cuda", dtype=torch.bfloat16).fill_(1.0)
     b = torch.empty_like(a)
     stream = torch.cuda.current_stream()
     for _ in range(3):
         b.copy_(a)
     reps = 20
     us = timed(lambda: b.copy_(a), reps, stream) / reps
+    del a, b
+    torch.cuda.empty_cache()
     return 2 * n * 2, us
 
 
@@ -474,6 +480,11 @@ def main():
         log("plain device copy, 64 MiB")
         cb, cus = bench_copy(args)
         extra["copy_64MiB"] = {"bytes_per_call": cb, "us": round(cus, 2), "GBps": round(cb / cus / 1e3, 1)}
+        log(f"  {cus:.1f} us, {cb / cus / 1e3:.0f} GB/s (read + write)")
+    if only and "copy1g" in only:
+        log("plain device copy, 1 GiB (beyond the last-level cache)")
+        cb, cus = bench_copy(args, 1024)
+        extra["copy_1GiB"] = {"bytes_per_call": cb, "us": round(cus, 2), "GBps": round(cb / cus / 1e3, 1)}
         log(f"  {cus:.1f} us, {cb / cus / 1e3:.0f} GB/s (read + write)")
     if want("oneshot"):
         log("one-shot, lockstep proxy")

@@ -41,24 +41,25 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // is aborted, so one load tells a workgroup both that it may go on and
   // whether to sum; it is never zero for a call (seq >= 1), the value the
   // word starts at.
-  const uint64_t seq = load_relaxed_agent(seq_dev) + 1u;
-  const uint32_t par = (uint32_t)seq & 1u;
-  uint16_t* const mine = a.send + (size_t)par * a.stride;
   const uint32_t nv = a.n >> 3, tail = a.n & 7u;
   const uint32_t tid = blockIdx.x * BLOCK + threadIdx.x;
   const uint32_t nthr = gridDim.x * BLOCK;
   const bool copier = blockIdx.x < a.ncopy;
   const bool keep_own = ONE_PASS && a.ncopy == gridDim.x;
 
+  // This rank's vector is loaded before the seq: only where it is stored
+  // depends on the parity, so the two loads are in flight together.
+  u32x4 own = {0u, 0u, 0u, 0u};
+  if (keep_own && tid < nv) own = ld16(a.in + 8u * (size_t)tid);
+  const uint64_t seq = load_relaxed_agent(seq_dev) + 1u;
+  const uint32_t par = (uint32_t)seq & 1u;
+  uint16_t* const mine = a.send + (size_t)par * a.stride;
+
   // 1. the first ncopy workgroups copy this rank's partial into send[par],
   //    each thread a stride of ncopy * BLOCK vectors
-  u32x4 own = {0u, 0u, 0u, 0u};
   if (copier) {
     if (keep_own) {
-      if (tid < nv) {
-        own = ld16(a.in + 8u * (size_t)tid);
-        st16(mine + 8u * (size_t)tid, own);
-      }
+      if (tid < nv) st16(mine + 8u * (size_t)tid, own);
     } else {
       const uint32_t cthr = a.ncopy * BLOCK;
       for (uint32_t v = tid; v < nv; v += cthr) st16(mine + 8u * (size_t)v, ld16(a.in + 8u * (size_t)v));
