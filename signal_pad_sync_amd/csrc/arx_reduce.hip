@@ -121,7 +121,9 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
         }
       }
       const bool bad = __any(!ok);
-      fence_acq_rel_system();
+      // a grid of one workgroup has nobody to release go to
+      if (single) fence_acquire_system();
+      else fence_acq_rel_system();
       if (threadIdx.x < kGoReplicas) store_relaxed_agent(go_word(a.words, threadIdx.x), (seq << 1) | (bad ? 1u : 0u));
       if (threadIdx.x == 0) {
         if (bad) report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
