@@ -297,14 +297,16 @@ def test_manual_publish_and_order():
         check_state(st, 0)
 
 
-def test_flag_timeout_is_latched():
+@pytest.mark.parametrize("W,n", [(2, 4096), (8, 131072), (4, 4194305)])
+def test_flag_timeout_is_latched(W, n):
     """No flag ever comes (manual mode, never published): the bounded wait
     runs out, the output stays untouched, counters still reset, seq advances,
-    and the next call reports the timeout."""
-    W, n = 2, 4096
+    and the next call reports the timeout. One workgroup (n = 4096), 32
+    workgroups all copying, and a grid-stride grid with half of them copying:
+    the others learn of the abort from the go word."""
     with library(W, n, mode=arx.PROXY_MANUAL, timeout_us=20000):
         inp, out = to_dev(np.ones(n, np.uint16)), sentinel(n)
-        note("forced flag timeout (20 ms)")
+        note(f"forced flag timeout (20 ms), W={W} n={n}")
         arx.allreduce(inp, out, n)
         torch.cuda.synchronize()
         assert np.all(to_host(out) == 0xDEAD)
