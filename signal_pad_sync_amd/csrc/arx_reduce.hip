@@ -36,11 +36,6 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   uint32_t* const cnt0 = a.words + WORD_CNT0;
   uint32_t* const cnt1 = a.words + WORD_CNT1;
 
-  // seq and parity: one more than the last completed call. seq is 64-bit
-  // like the host's flags. The go word holds 2 * seq, plus 1 when the call
-  // is aborted, so one load tells a workgroup both that it may go on and
-  // whether to sum; it is never zero for a call (seq >= 1), the value the
-  // word starts at.
   const uint32_t nv = a.n >> 3, tail = a.n & 7u;
   const uint32_t tid = blockIdx.x * BLOCK + threadIdx.x;
   const uint32_t nthr = gridDim.x * BLOCK;
@@ -51,6 +46,12 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // depends on the parity, so the two loads are in flight together.
   u32x4 own = {0u, 0u, 0u, 0u};
   if (keep_own && tid < nv) own = ld16(a.in + 8u * (size_t)tid);
+
+  // seq and parity: one more than the last completed call. seq is 64-bit
+  // like the host's flags. The go word holds 2 * seq, plus 1 when the call
+  // is aborted, so one load tells a workgroup both that it may go on and
+  // whether to sum; it is never zero for a call (seq >= 1), the value the
+  // word starts at.
   const uint64_t seq = load_relaxed_agent(seq_dev) + 1u;
   const uint32_t par = (uint32_t)seq & 1u;
   uint16_t* const mine = a.send + (size_t)par * a.stride;
