@@ -77,16 +77,19 @@ def parse():
 GATE_CYCLES = 200_000_000
 
 
-def timed(fn, steps, stream, gate=False):
-    """Event time of `steps` calls of fn on `stream`, in microseconds. With
-    gate, a spin kernel ahead of the start event keeps the GPU busy while
-    the host enqueues the calls (for launches shorter than the host's
-    enqueue cost)."""
+def timed(fn, steps, stream, gate=False, warmup=0):
+    """Event time of `steps` calls of fn on `stream`, in microseconds, after
+    `warmup` untimed calls. With gate, a spin kernel ahead of the warm-up
+    calls keeps the GPU busy while the host enqueues every call (for
+    launches shorter than the host's enqueue cost); the warm-up calls then
+    run on the GPU right before the timed ones, with no idle time between."""
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     if gate and hasattr(torch.cuda, "_sleep"):   # without it the timing is merely ungated
         torch.cuda._sleep(GATE_CYCLES)
+    for _ in range(warmup):
+        fn()
     start.record(stream)
     for _ in range(steps):
         fn()
@@ -127,9 +130,14 @@ def bench_oneshot(args, mode, graph=False):
             call, xp, op, sh = arx.lib.arx_allreduce, x.data_ptr(), out.data_ptr(), stream.cuda_stream
             rcs = []
             fn, reps = (lambda: rcs.append(call(xp, op, n, sh))), args.steps
-        for _ in range(max(1, args.warmup // per)):
-            fn()
-        us = timed(fn, reps, stream, gate=not graph)
+        if graph:
+            for _ in range(max(1, args.warmup // per)):
+                fn()
+            us = timed(fn, reps, stream)
+        else:
+            fn()                       # the first call's one-time host set-up, outside the gate
+            torch.cuda.synchronize()
+            us = timed(fn, reps, stream, gate=True, warmup=max(1, args.warmup))
         calls = reps * per
         if not graph:
             assert not any(rcs), f"arx_allreduce failed: {set(rcs)}"
@@ -159,9 +167,9 @@ def bench_launch_floor(args):
         call, xp, op, sh = arx.lib.arx_reduce, x.data_ptr(), out.data_ptr(), stream.cuda_stream
         rcs = []
         fn = lambda: rcs.append(call(xp, op, n, 0, sh))
-        for _ in range(args.warmup):
-            fn()
-        us = timed(fn, args.steps, stream, gate=True) / args.steps
+        fn()
+        torch.cuda.synchronize()
+        us = timed(fn, args.steps, stream, gate=True, warmup=max(1, args.warmup)) / args.steps
         assert not any(rcs), f"arx_reduce failed: {set(rcs)}"
     finally:
         torch.cuda.synchronize()
