@@ -43,9 +43,12 @@ def kernel_source_hash(csrc=os.path.join(ROOT, "signal_pad_sync_amd", "csrc")):
 
 
 def recorded_traffic(key, path=os.path.join(ROOT, "profiles", "hbm_traffic.json"), csrc=None):
-    """HBM bytes per launch measured by the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs summarised in profiles/hbm_traffic_pmc.md, or None when the kernel
-    sources have changed since those counters were taken."""
+    """HBM bytes per launch recorded from the rocprofv3 counter runs
+    summarised in profiles/hbm_traffic_pmc.md (FETCH_SIZE scaled by what a
+    plain copy of known size reads on it, plus WRITE_SIZE; or, under the
+    keys ending in _by_request_size, the read and write request counts by
+    size), or None when the kernel sources have changed since those counters
+    were taken."""
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -470,6 +473,7 @@ def make_line(args, us_call, cpu, extra):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
                      "traffic": recorded_traffic("oneshot_kernel_w8_n131072_bytes"),
+                     "traffic_by_request_size": recorded_traffic("oneshot_kernel_w8_n131072_bytes_by_request_size"),
                      "kernel": "oneshot_kernel<8,true,512>", "bytes_per_launch": bytes_call,
                      "event_us_per_launch": round(us_call, 3) if us_call else None},
         "cpu_baseline": cpu,
@@ -531,7 +535,8 @@ def main():
             "bytes_per_call": rb, "us_median_single": round(med, 2),
             "us_median_single_after_cache_sweep": round(med_scrub, 2), "us_mean_back_to_back": round(mean, 2),
             "GBps": round(rb / mean / 1e3, 1), "frac_of_hbm_peak": round(rb / mean / 1e3 / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("reduce_kernel_w8_n67108864_bytes")}
+            "traffic": recorded_traffic("reduce_kernel_w8_n67108864_bytes"),
+            "traffic_by_request_size": recorded_traffic("reduce_kernel_w8_n67108864_bytes_by_request_size")}
         log(f"  {mean:.1f} us per launch back to back ({med:.1f} us median timed one by one), "
             f"{rb / mean / 1e3:.0f} GB/s")
     if want("barrier"):

@@ -34,10 +34,10 @@ extern "C" {
 int arx_debug_state(uint64_t* words, int nwords);
 
 /* Test aid: set the protocol's state as if `seq` calls had completed
- * (device seq and go, ctl.seq, ctl.done, the proxy's posted seq and every
- * peer flag), so tests can reach large sequence numbers. Waits for the
- * device; allowed in the lockstep and manual modes only, with no call in
- * flight. Errors: ARX_ESTATE, ARX_EHIP. */
+ * (the device's seq, go and published words, ctl.seq, ctl.done, the proxy's
+ * posted seq and every peer flag), so tests can reach large sequence
+ * numbers. Waits for the device; allowed in the lockstep and manual modes
+ * only, with no call in flight. Errors: ARX_ESTATE, ARX_EHIP. */
 int arx_debug_set_seq(uint64_t seq);
 
 /* Test aid: the proxy's next post in ARX_PROXY_STRESS mode fails, as a

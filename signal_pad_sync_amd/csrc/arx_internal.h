@@ -43,10 +43,13 @@ enum : int {
   WORD_CNT1 = 128,   // workgroups finished (finish counter)
   WORD_GO = 192,     // go (u64): 2 * seq of the call whose peer data has all arrived, + 1 if that call
                      // is aborted; kGoReplicas copies, WORD_GO + 64 * k for replica k
+  WORD_PUBLISHED = 704,  // seq (u64) of the last call whose seq was published to the proxy: a hint
+                         // that tells workgroup 0 when to start reading the peers' flags
   WORDS_TOTAL = 1024,
 };
 constexpr int kGoReplicas = 8;
-static_assert(WORD_GO + 64 * kGoReplicas <= WORDS_TOTAL, "go replicas fit in the word block");
+static_assert(WORD_GO + 64 * kGoReplicas <= WORD_PUBLISHED, "go replicas fit below the published word");
+static_assert(WORD_PUBLISHED + 64 <= WORDS_TOTAL, "the published word fits in the word block");
 
 constexpr int kBlock = 256;       // threads per workgroup of the reduction kernels
 constexpr int kMaxOneShotGrid = 256;  // co-resident workgroups of the one-shot kernel

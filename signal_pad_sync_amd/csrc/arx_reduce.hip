@@ -33,6 +33,7 @@ template <int W, bool ONE_PASS, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   __shared__ uint32_t s_abort;
   uint64_t* const seq_dev = reinterpret_cast<uint64_t*>(a.words + WORD_SEQ);
+  uint64_t* const published = reinterpret_cast<uint64_t*>(a.words + WORD_PUBLISHED);
   uint32_t* const cnt0 = a.words + WORD_CNT0;
   uint32_t* const cnt1 = a.words + WORD_CNT1;
 
@@ -72,8 +73,9 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // 2. arrival count: one system-scope release per copying workgroup
   //    carries all its waves' copies (they precede it through the workgroup
   //    barrier); the last to arrive acquires them all, resets the counter
-  //    and publishes seq to the host proxy. A grid of one workgroup is its
-  //    own last arrival: its release store of seq carries the copies.
+  //    and publishes seq to the host proxy, then tells workgroup 0 so in
+  //    the published word. A grid of one workgroup is its own last arrival:
+  //    its release store of seq carries the copies.
   const bool single = gridDim.x == 1u;
   if (single && threadIdx.x == 0) {
     store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
@@ -84,6 +86,7 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
       store_relaxed_agent(cnt0, 0u);
       store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
       store_release_system(&a.ctl->seq, seq);
+      store_relaxed_agent(published, seq);
     }
   }
 
@@ -101,7 +104,13 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // 3. flag wait, then go (page "arx.cu", protocol comment: only one block
   //    reads the peers' flags, the others learn of them from device
   //    memory). In workgroup 0, the lane of each peer rank reads that peer's
-  //    pinned flag over PCIe until it reaches seq. The wave then takes one
+  //    pinned flag over PCIe once; if the flag is short of seq (the peer is
+  //    not ahead), the lane waits until the published word reaches seq and
+  //    only then reads the flag again until it does. Flag reads in flight
+  //    delay the GPU's own store of seq to pinned memory, which the proxy
+  //    (and every peer) waits for: polling from the arrival on made a
+  //    lockstep 256 KiB call 0.4-0.5 us slower. The published word is a
+  //    hint only: what lets the wave on is the flag. The wave then takes one
   //    fence that both acquires what the flags publish and releases it
   //    further, and its first 8 lanes store the go value into 8 replicas of
   //    the go word, one 256-byte line each; workgroup b polls replica b % 8,
@@ -113,7 +122,11 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
       bool ok = true;
       if ((int)threadIdx.x < W && (int)threadIdx.x != a.rank) {
         const uint64_t t0 = now_ticks();
-        while (load_relaxed_system(a.flags + threadIdx.x) < seq) {
+        const bool ahead = load_relaxed_system(a.flags + threadIdx.x) >= seq;
+        if (!ahead && !single)
+          while (load_relaxed_agent(published) < seq && now_ticks() - t0 <= a.timeout)
+            __builtin_amdgcn_s_sleep(1);
+        while (!ahead && load_relaxed_system(a.flags + threadIdx.x) < seq) {
           if (now_ticks() - t0 > a.timeout) {
             ok = false;
             break;

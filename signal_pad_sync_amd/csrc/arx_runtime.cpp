@@ -528,6 +528,7 @@ int arx_debug_set_seq(uint64_t seq) {
   const uint64_t go = seq << 1;
   for (int k = 0; k < arx::kGoReplicas; ++k)
     HIPCHK(hipMemcpy(S.words + arx::WORD_GO + 64 * k, &go, sizeof go, hipMemcpyHostToDevice));
+  HIPCHK(hipMemcpy(S.words + arx::WORD_PUBLISHED, &seq, sizeof seq, hipMemcpyHostToDevice));
   store_release(&S.ctl->done, seq);
   store_release(&S.ctl->seq, seq);
   S.core->reset(seq);
