@@ -144,8 +144,9 @@ int arx_publish(uint64_t seq);
  * If this call's own flag wait times out on the device, out is left
  * untouched, seq still advances and the error is latched for the next call.
  * The kernel's workgroups wait on each other, so its grid never exceeds
- * what the device holds at once (occupancy per CU times the CU count, at
- * most 256 workgroups); past one vector per thread, threads loop.
+ * what the device holds at once (occupancy per CU times the CU count: at
+ * most 256 workgroups that reduce and one that waits for the flags); past
+ * one vector per thread, threads loop.
  */
 int arx_allreduce(const void* in, void* out, size_t n, hipStream_t stream);
 

@@ -160,6 +160,7 @@ MUTANTS = {
     "M6": "the arrival count publishes one copying workgroup early",
     "M7": "with early_finish, workgroup 0 also counts itself finished before its flag wait",
     "M8": "with early_finish, a workgroup other than 0 counts itself finished before it reads the seq",
+    "M9": "workgroup 0 gives go once this rank has published the seq, without the peers' flags",
 }
 
 
@@ -177,7 +178,8 @@ class CheckResult:
 
 def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                    max_states: int = 5_000_000, copiers: Optional[int] = None,
-                   early_finish: bool = False) -> CheckResult:
+                   early_finish: bool = False, poller: bool = False,
+                   go_after_publish: bool = False) -> CheckResult:
     """Explores every interleaving of W ranks x G workgroups x S calls.
 
     copiers: the number C of workgroups that copy and count arrival (default
@@ -203,6 +205,18 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
     last workgroup to count records seq s as finished, workgroup 0 has passed
     its flag wait for s.
 
+    poller: workgroup 0 only waits for the flags and gives go (page "arx.cu",
+    protocol comment: one block reads the flags); it neither copies nor
+    reduces and has no slice. Workgroups 1 .. G-1 hold the slices; the first
+    C of them copy (workgroup 1 + k copies every slice 1 + i with i % C ==
+    k; C defaults to G - 1) and count arrival, and all of them wait for go
+    and reduce. Workgroup 0 reads the seq, waits for the flags (possibly
+    before any arrival: a peer may be ahead) and counts itself finished
+    (M7: before its wait).
+
+    go_after_publish: workgroup 0's wait also needs this rank's own publish
+    of the seq (the kernel's rule past a few vectors per copying thread).
+
     Rank state tuple: (c, pcs, ss, cnt0, cnt1, go, seq_dev, ctl_seq, done,
     send, recv, flag, posted, pcur, ppos) where c is the running call (S + 1
     after the last), pcs/ss the per-workgroup program counter and seq,
@@ -214,9 +228,12 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
         raise ValueError(mutant)
     if mutant in ("M7", "M8") and not early_finish:
         raise ValueError(f"{mutant} is a mutant of early_finish")
-    C = G if copiers is None else copiers
-    if not 1 <= C <= G:
-        raise ValueError(f"copiers {C} not in [1, {G}]")
+    if poller and G < 2:
+        raise ValueError("a poll workgroup needs at least one reducing workgroup")
+    first = 1 if poller else 0          # the first workgroup that holds a slice
+    C = G - first if copiers is None else copiers
+    if not 1 <= C <= G - first:
+        raise ValueError(f"copiers {C} not in [1, {G - first}]")
     if mutant == "M6" and C < 2:
         raise ValueError("M6 needs at least two copying workgroups")
     last_arrival = C - 2 if mutant == "M6" else C - 1
@@ -230,7 +247,9 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
         return LASTOUT if (mutant == "M8" and g != 0) else READSEQ
 
     def after_seq(g):
-        if g < C:
+        if poller and g == 0:
+            return LASTOUT if mutant == "M7" else WAIT
+        if first <= g < first + C:
             return COPY
         return LASTOUT if (early_finish and g != 0 and mutant != "M8") else WAIT
 
@@ -240,6 +259,8 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
         return WAIT
 
     def after_lastout(g):
+        if poller and g == 0:
+            return WAIT if mutant == "M7" else DONE
         if not early_finish:
             return DONE
         if g == 0:
@@ -258,7 +279,7 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
         acts = []
         for step in range(1, W):
             j = (r + step) % W
-            data = [("data", j, g) for g in range(G)]
+            data = [("data", j, g) for g in range(first, G)]
             flag = [("flag", j, 0)]
             acts += (flag + data) if mutant == "M3" else (data + flag)
         return acts
@@ -295,7 +316,7 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                               cnt0, cnt1, go, seq_dev, ctl_seq, done, send, recv, flag, posted, pcur, ppos)
                     elif pc == COPY:
                         send2 = list(send)
-                        for g2 in range(g, G, C):
+                        for g2 in range(g, G, C):   # copier g: slices g, g + C, ...
                             send2[par_of(s) * G + g2] = _tag(r, s)
                         send2 = tuple(send2)
                         ns = (c, pcs[:g] + (ARRIVE,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
@@ -316,8 +337,14 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                                   done, send, recv, flag, posted, pcur, ppos)
                     elif pc == WAIT:
                         if g == 0:
-                            if all(flag[j] >= s for j in range(W) if j != r):
-                                nxt = LASTOUT if (early_finish and mutant != "M7") else REDUCE
+                            flags_in = all(flag[j] >= s for j in range(W) if j != r)
+                            if go_after_publish:
+                                flags_in = flags_in and ctl_seq >= s
+                            if (ctl_seq >= s) if mutant == "M9" else flags_in:
+                                if poller:
+                                    nxt = DONE if mutant == "M7" else LASTOUT
+                                else:
+                                    nxt = LASTOUT if (early_finish and mutant != "M7") else REDUCE
                                 ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss, cnt0, cnt1, s, seq_dev,
                                       ctl_seq, done, send, recv, flag, posted, pcur, ppos)
                         elif mutant == "M5" or go >= s:

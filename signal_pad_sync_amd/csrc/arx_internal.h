@@ -29,7 +29,7 @@ static_assert(sizeof(Ctl) == 192, "Ctl layout");
 
 enum : uint64_t {
   ERR_NONE = 0,
-  ERR_FLAG_TIMEOUT = 1,     // workgroup 0 gave up waiting for a peer flag
+  ERR_FLAG_TIMEOUT = 1,     // the flag wait gave up waiting for a peer flag
   ERR_GO_TIMEOUT = 2,       // a workgroup gave up waiting for go
   ERR_BARRIER_TIMEOUT = 3,  // a signal-pad CAS wait gave up
   ERR_COUNTER_TIMEOUT = 4,  // a counter-barrier wait gave up
@@ -44,7 +44,7 @@ enum : int {
   WORD_GO = 192,     // go (u64): 2 * seq of the call whose peer data has all arrived, + 1 if that call
                      // is aborted; kGoReplicas copies, WORD_GO + 64 * k for replica k
   WORD_PUBLISHED = 704,  // seq (u64) of the last call whose seq was published to the proxy: a hint
-                         // that tells workgroup 0 when to start reading the peers' flags
+                         // that tells the flag wait when to read the peers' flags again
   WORDS_TOTAL = 1024,
 };
 constexpr int kGoReplicas = 8;
@@ -52,7 +52,7 @@ static_assert(WORD_GO + 64 * kGoReplicas <= WORD_PUBLISHED, "go replicas fit bel
 static_assert(WORD_PUBLISHED + 64 <= WORDS_TOTAL, "the published word fits in the word block");
 
 constexpr int kBlock = 256;       // threads per workgroup of the reduction kernels
-constexpr int kMaxOneShotGrid = 256;  // co-resident workgroups of the one-shot kernel
+constexpr int kMaxOneShotGrid = 256;  // reducing workgroups of the one-shot kernel, at most
 
 struct OneShotArgs {
   const uint16_t* in;
@@ -67,6 +67,7 @@ struct OneShotArgs {
   int rank;
   uint64_t timeout;        // wall-clock ticks per wait
   uint32_t ncopy;          // workgroups that copy and count arrival (set by the launcher)
+  uint32_t early_go;       // 1: go may precede this rank's publish (set by the launcher)
 };
 
 struct ReduceArgs {
@@ -142,9 +143,10 @@ hipError_t launch_round_test(const uint32_t* in, uint16_t* out, size_t n, hipStr
 // (defined in arx_runtime.cpp).
 int set_error(int code, const char* fmt, ...);
 
-// Grid the one-shot kernel uses for n elements with `block` threads per
-// workgroup, at most max_grid (all its workgroups must be resident at once,
-// since they wait on each other).
+// Reducing workgroups the one-shot kernel uses for n elements with `block`
+// threads per workgroup, at most max_grid (all its workgroups must be
+// resident at once, since they wait on each other; a grid of more than one
+// adds the poll workgroup).
 unsigned oneshot_grid(uint32_t n, int block, unsigned max_grid);
 // Workgroups of a one-shot grid that copy the partial and count arrival.
 unsigned oneshot_copiers(unsigned grid);

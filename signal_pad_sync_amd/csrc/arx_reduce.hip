@@ -1,8 +1,8 @@
 // arx_reduce.hip — the reduction kernels of libarx for gfx950.
 //
 //   oneshot_kernel     one call of the one-shot path: copy into the send
-//                      slot, arrival count and publish, flag wait in
-//                      workgroup 0, go broadcast, W-way reduction,
+//                      slot, arrival count and publish, flag wait in a
+//                      poll workgroup, go broadcast, W-way reduction,
 //                      last-block-out (page "arx.cu", arx_kernel)
 //   reduce_kernel      the W-way reduction alone, streaming from HBM
 //   round_test_kernel  the reduction's binary32 -> bf16 rounding alone
@@ -22,13 +22,22 @@ namespace arx {
 
 // ---- one-shot kernel --------------------------------------------------------
 
-// ONE_PASS: the grid has a thread for every 16-byte vector. When every
-// workgroup copies (ncopy == gridDim.x), each thread keeps its own
-// partial's vector in registers from the copy to the sum.
-// Only the first ncopy workgroups copy and count arrival; every workgroup
-// waits for go and reduces, reading its own partial from `in` (the send
-// slot is what the peers receive, and its copy is complete before the
-// publish). ncopy < gridDim.x only when `in` and `out` do not overlap.
+// A grid of more than one workgroup has a poll workgroup and G = gridDim.x - 1
+// reducing workgroups. The poll workgroup (blockIdx 0, dispatched first)
+// only reads the peers' flags and releases go (page "arx.cu", protocol
+// comment: only one block reads the flags, the others learn of them from
+// device memory); it neither copies nor reduces, so its reads over PCIe hold
+// up no copy, and a peer that is already ahead is seen about one PCIe read
+// after the kernel starts. Reducing workgroup r = blockIdx.x - 1 copies (if
+// r < ncopy), counts arrival, waits for go and sums its share of vectors.
+// A grid of one workgroup does every step itself.
+//
+// ONE_PASS: the G reducing workgroups have a thread for every 16-byte
+// vector. When every one of them copies (ncopy == G), each thread keeps
+// its own partial's vector in registers from the copy to the sum. Every
+// reducing workgroup reads its own partial from `in` (the send slot is what
+// the peers receive, and its copy is complete before the publish). ncopy <
+// G only when `in` and `out` do not overlap.
 template <int W, bool ONE_PASS, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   __shared__ uint32_t s_abort;
@@ -36,12 +45,65 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   uint64_t* const published = reinterpret_cast<uint64_t*>(a.words + WORD_PUBLISHED);
   uint32_t* const cnt0 = a.words + WORD_CNT0;
   uint32_t* const cnt1 = a.words + WORD_CNT1;
+  const bool single = gridDim.x == 1u;
 
+  // ---- the poll workgroup: its first wave only
+  if (!single && blockIdx.x == 0) {
+    if (threadIdx.x >= 64) return;
+    const uint32_t lane = threadIdx.x;
+    const bool peer = (int)lane < W && (int)lane != a.rank;
+    // The lane of each peer rank reads that peer's pinned flag once, at
+    // once (in flight with the seq load). If the peer is not yet at seq,
+    // the lane waits until the published word says this rank has published
+    // seq, and only then reads the flag again until it reaches seq: flag
+    // reads in flight around the GPU's store of seq to pinned memory, which
+    // the proxy (and every peer) waits for, delay that store on some hosts.
+    // The published word is a hint only: what lets the wave on is the flag.
+    // Without early_go the wave also waits for the published word when the
+    // flag was already there, so go never precedes the publish.
+    uint64_t f = 0;
+    if (peer) f = load_relaxed_system(a.flags + lane);
+    const uint64_t seq = load_relaxed_agent(seq_dev) + 1u;
+    bool ok = true;
+    if (peer && (f < seq || !a.early_go)) {
+      const uint64_t t0 = now_ticks();
+      while (load_relaxed_agent(published) < seq && now_ticks() - t0 <= a.timeout) __builtin_amdgcn_s_sleep(1);
+      while (f < seq && load_relaxed_system(a.flags + lane) < seq) {
+        if (now_ticks() - t0 > a.timeout) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    // One fence acquires what the flags publish and releases it further;
+    // the first 8 lanes then store the go value into 8 replicas of the go
+    // word, one 256-byte line each. Reducing workgroup b polls replica
+    // b % 8, so the workgroups of each XCD (dealt round robin) share a line.
+    const bool bad = __any(!ok);
+    fence_acq_rel_system();
+    if (lane < kGoReplicas) store_relaxed_agent(go_word(a.words, lane), (seq << 1) | (bad ? 1u : 0u));
+    if (lane == 0) {
+      if (bad) report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
+      // the finish count, after the flag wait (see below); the last
+      // workgroup to count records the call as finished
+      if (fetch_add_relaxed_agent(cnt1, 1u) == gridDim.x - 1u) {
+        store_relaxed_agent(cnt1, 0u);
+        store_relaxed_agent(seq_dev, seq);
+        store_relaxed_system(&a.ctl->done, seq);
+      }
+    }
+    return;
+  }
+
+  // ---- the reducing workgroups (or the single one)
+  const uint32_t nred = single ? 1u : gridDim.x - 1u;
+  const uint32_t r = single ? 0u : blockIdx.x - 1u;
   const uint32_t nv = a.n >> 3, tail = a.n & 7u;
-  const uint32_t tid = blockIdx.x * BLOCK + threadIdx.x;
-  const uint32_t nthr = gridDim.x * BLOCK;
-  const bool copier = blockIdx.x < a.ncopy;
-  const bool keep_own = ONE_PASS && a.ncopy == gridDim.x;
+  const uint32_t tid = r * BLOCK + threadIdx.x;
+  const uint32_t nthr = nred * BLOCK;
+  const bool copier = r < a.ncopy;
+  const bool keep_own = ONE_PASS && a.ncopy == nred;
 
   // This rank's vector is loaded before the seq: only where it is stored
   // depends on the parity, so the two loads are in flight together.
@@ -57,8 +119,8 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   const uint32_t par = (uint32_t)seq & 1u;
   uint16_t* const mine = a.send + (size_t)par * a.stride;
 
-  // 1. the first ncopy workgroups copy this rank's partial into send[par],
-  //    each thread a stride of ncopy * BLOCK vectors
+  // 1. the first ncopy reducing workgroups copy this rank's partial into
+  //    send[par], each thread a stride of ncopy * BLOCK vectors
   if (copier) {
     if (keep_own) {
       if (tid < nv) st16(mine + 8u * (size_t)tid, own);
@@ -73,10 +135,9 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // 2. arrival count: one system-scope release per copying workgroup
   //    carries all its waves' copies (they precede it through the workgroup
   //    barrier); the last to arrive acquires them all, resets the counter
-  //    and publishes seq to the host proxy, then tells workgroup 0 so in
-  //    the published word. A grid of one workgroup is its own last arrival:
-  //    its release store of seq carries the copies.
-  const bool single = gridDim.x == 1u;
+  //    and publishes seq to the host proxy, then tells the poll workgroup so
+  //    in the published word. A grid of one workgroup is its own last
+  //    arrival: its release store of seq carries the copies.
   if (single && threadIdx.x == 0) {
     store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
     store_release_system(&a.ctl->seq, seq);
@@ -92,41 +153,26 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
 
   // The finish count. It has to follow every workgroup's read of seq_dev
   // (the last workgroup to count advances it) and, so that the recorded
-  // finished seq means the peers' flags were seen, workgroup 0's flag wait;
-  // nothing else. So workgroups other than 0 count themselves finished here,
-  // where their atomic overlaps the flag round trip, and workgroup 0 right
-  // after its flag wait; the last to count is then nearly always workgroup
-  // 0, uncontended. (On the page every block counts after its reduction;
-  // moving the count took 0.8-1.0 us off a 256 KiB call on MI355X.)
+  // finished seq means the peers' flags were seen, the flag wait; nothing
+  // else. So the reducing workgroups count themselves finished here, where
+  // their atomic overlaps the flag round trip, and the poll workgroup right
+  // after its flag wait; the last to count is then nearly always the poll
+  // workgroup, uncontended. (On the page every block counts after its
+  // reduction; moving the count took 0.8-1.0 us off a 256 KiB call on
+  // MI355X.)
   uint32_t finished = 0;
-  if (!single && blockIdx.x != 0 && threadIdx.x == 0) finished = fetch_add_relaxed_agent(cnt1, 1u);
+  if (!single && threadIdx.x == 0) finished = fetch_add_relaxed_agent(cnt1, 1u);
 
-  // 3. flag wait, then go (page "arx.cu", protocol comment: only one block
-  //    reads the peers' flags, the others learn of them from device
-  //    memory). In workgroup 0, the lane of each peer rank reads that peer's
-  //    pinned flag over PCIe once; if the flag is short of seq (the peer is
-  //    not ahead), the lane waits until the published word reaches seq and
-  //    only then reads the flag again until it does. Flag reads in flight
-  //    delay the GPU's own store of seq to pinned memory, which the proxy
-  //    (and every peer) waits for: polling from the arrival on made a
-  //    lockstep 256 KiB call 0.4-0.5 us slower. The published word is a
-  //    hint only: what lets the wave on is the flag. The wave then takes one
-  //    fence that both acquires what the flags publish and releases it
-  //    further, and its first 8 lanes store the go value into 8 replicas of
-  //    the go word, one 256-byte line each; workgroup b polls replica b % 8,
-  //    so the workgroups of each XCD (dealt round robin) share a line and no
-  //    line has more than a few pollers.
+  // 3. a grid of one workgroup waits for the flags itself (its first wave,
+  //    one lane per peer); the reducing workgroups of a larger grid wait for
+  //    go from the poll workgroup, then take an agent-scope acquire
   bool abort;
-  if (blockIdx.x == 0) {
+  if (single) {
     if (threadIdx.x < 64) {
       bool ok = true;
       if ((int)threadIdx.x < W && (int)threadIdx.x != a.rank) {
         const uint64_t t0 = now_ticks();
-        const bool ahead = load_relaxed_system(a.flags + threadIdx.x) >= seq;
-        if (!ahead && !single)
-          while (load_relaxed_agent(published) < seq && now_ticks() - t0 <= a.timeout)
-            __builtin_amdgcn_s_sleep(1);
-        while (!ahead && load_relaxed_system(a.flags + threadIdx.x) < seq) {
+        while (load_relaxed_system(a.flags + threadIdx.x) < seq) {
           if (now_ticks() - t0 > a.timeout) {
             ok = false;
             break;
@@ -135,18 +181,15 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
         }
       }
       const bool bad = __any(!ok);
-      // a grid of one workgroup has nobody to release go to
-      if (single) fence_acquire_system();
-      else fence_acq_rel_system();
+      fence_acquire_system();   // nobody to release to
       if (threadIdx.x < kGoReplicas) store_relaxed_agent(go_word(a.words, threadIdx.x), (seq << 1) | (bad ? 1u : 0u));
       if (threadIdx.x == 0) {
         if (bad) report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
-        if (!single) finished = fetch_add_relaxed_agent(cnt1, 1u);
         s_abort = bad ? 1u : 0u;
       }
     }
-    // the other waves of workgroup 0 are ordered after the polling wave's
-    // acquire by the workgroup barrier
+    // the other waves are ordered after the first wave's acquire by the
+    // workgroup barrier
     __syncthreads();
     abort = s_abort != 0u;
   } else {
@@ -236,8 +279,9 @@ unsigned oneshot_grid(uint32_t n, int block, unsigned max_grid) {
 }
 
 // Workgroups of oneshot_kernel<W, ONE_PASS, BLOCK> that fit on the device at
-// once: its occupancy per CU times the CU count, at most kMaxOneShotGrid; 0
-// if the occupancy query fails. The occupancy is queried once per variant.
+// once: its occupancy per CU times the CU count, at most kMaxOneShotGrid + 1
+// (the reducing workgroups and the poll workgroup); 0 if the occupancy query
+// fails. The occupancy is queried once per variant.
 template <int W, bool ONE_PASS, int BLOCK>
 static unsigned coresident(int cus) {
   static const int per_cu = [] {
@@ -248,7 +292,7 @@ static unsigned coresident(int cus) {
                : 0;
   }();
   const long long cap = (long long)per_cu * cus;
-  return (unsigned)(cap < kMaxOneShotGrid ? cap : kMaxOneShotGrid);
+  return (unsigned)(cap < kMaxOneShotGrid + 1 ? cap : kMaxOneShotGrid + 1);
 }
 
 template <int W, int BLOCK>
@@ -256,23 +300,33 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   // every workgroup waits on the others, so all must be resident together
   const unsigned cap = coresident<W, false, BLOCK>(cus);
   const unsigned cap1 = coresident<W, true, BLOCK>(cus);
-  const unsigned max_grid = cap < cap1 ? cap : cap1;
-  if (max_grid == 0) return hipErrorInvalidConfiguration;
-  const unsigned grid = oneshot_grid(a.n, BLOCK, max_grid);
+  const unsigned resident = cap < cap1 ? cap : cap1;
+  if (resident == 0) return hipErrorInvalidConfiguration;
+  // grid: the reducing workgroups; one more polls the flags when there are
+  // several, so all of them fit in resident - 1 (or make a grid of one)
+  const unsigned grid = oneshot_grid(a.n, BLOCK, resident > 1 ? resident - 1 : 1);
   const bool one_pass = (a.n >> 3) <= grid * (uint32_t)BLOCK;
-  // With out == in, every workgroup copies: each thread then copies a vector
-  // before it reduces (and overwrites) it. Were other workgroups copying,
-  // go could come before their copy (go follows the peers' flags, which a
-  // peer running ahead posts before this rank publishes) and the send slot
-  // would get the output instead of the input.
+  // With out == in, every reducing workgroup copies: each thread then
+  // copies a vector before it reduces (and overwrites) it. Were other
+  // workgroups copying, go could come before their copy (go follows the
+  // peers' flags, which a peer running ahead posts before this rank
+  // publishes) and the send slot would get the output instead of the input.
   const uint64_t ib = (uint64_t)(uintptr_t)a.in, ob = (uint64_t)(uintptr_t)a.out, nb = 2ull * a.n;
   const bool disjoint = ib + nb <= ob || ob + nb <= ib;
   OneShotArgs b = a;
   b.ncopy = disjoint ? oneshot_copiers(grid) : grid;
+  // Go before the publish (a peer ahead) lets the workgroups that do not
+  // copy reduce while the copiers copy; past 4 vectors copied per copying
+  // thread the copiers then finish alone, and the call gets slower than
+  // with go after the publish (W=8, run-ahead peers, n = 16 Mi: 84.6 against
+  // 75.9 us; at n = 4 Mi, 2 vectors per reducing thread, early go is 1.8 us
+  // faster). So early go is allowed up to 4 vectors per copying thread.
+  b.early_go = ((a.n >> 3) + b.ncopy * BLOCK - 1) / (b.ncopy * BLOCK) <= 4u ? 1u : 0u;
+  const unsigned launched = grid > 1 ? grid + 1 : 1;
   if (one_pass)
-    hipLaunchKernelGGL((oneshot_kernel<W, true, BLOCK>), dim3(grid), dim3(BLOCK), 0, s, b);
+    hipLaunchKernelGGL((oneshot_kernel<W, true, BLOCK>), dim3(launched), dim3(BLOCK), 0, s, b);
   else
-    hipLaunchKernelGGL((oneshot_kernel<W, false, BLOCK>), dim3(grid), dim3(BLOCK), 0, s, b);
+    hipLaunchKernelGGL((oneshot_kernel<W, false, BLOCK>), dim3(launched), dim3(BLOCK), 0, s, b);
   return hipGetLastError();
 }
 

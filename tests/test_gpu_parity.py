@@ -230,8 +230,8 @@ def test_reduce_only_empty():
 
 def test_grid_stride_path():
     """n beyond one vector per thread of the largest co-resident grid
-    (256 workgroups x 1024 threads x 8 elements = 2 Mi), so each thread
-    loops over several vectors; ragged tail included."""
+    (256 reducing workgroups x 1024 threads x 8 elements = 2 Mi), so each
+    thread loops over several vectors; ragged tail included."""
     W, rank = 3, 2
     max_n = (1 << 22) + 64
     recv = [[WL.normal(7000 + 10 * par + s, max_n) for s in range(W)] for par in (0, 1)]
