@@ -161,6 +161,7 @@ MUTANTS = {
     "M7": "with early_finish, workgroup 0 also counts itself finished before its flag wait",
     "M8": "with early_finish, a workgroup other than 0 counts itself finished before it reads the seq",
     "M9": "workgroup 0 gives go once this rank has published the seq, without the peers' flags",
+    "M10": "with poll_arrives, the poll workgroup counts itself finished before its arrival wave has arrived",
 }
 
 
@@ -179,7 +180,7 @@ class CheckResult:
 def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                    max_states: int = 5_000_000, copiers: Optional[int] = None,
                    early_finish: bool = False, poller: bool = False,
-                   go_after_publish: bool = False) -> CheckResult:
+                   go_after_publish: bool = False, poll_arrives: bool = False) -> CheckResult:
     """Explores every interleaving of W ranks x G workgroups x S calls.
 
     copiers: the number C of workgroups that copy and count arrival (default
@@ -217,6 +218,15 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
     go_after_publish: workgroup 0's wait also needs this rank's own publish
     of the seq (the kernel's rule past a few vectors per copying thread).
 
+    poll_arrives: the poll workgroup also counts one arrival (it stores the
+    call's size for the proxy before it), from a wave of its own that runs
+    beside its flag wait: one more process, which reads the seq and arrives
+    and does nothing else; the publish then comes with the (C + 1)-th
+    arrival, whichever process makes it. The poll workgroup counts itself
+    finished only once that wave has arrived: otherwise, with a peer ahead,
+    the call can be recorded finished before the wave reads the seq, and it
+    then arrives for the next call and publishes it (M10).
+
     Rank state tuple: (c, pcs, ss, cnt0, cnt1, go, seq_dev, ctl_seq, done,
     send, recv, flag, posted, pcur, ppos) where c is the running call (S + 1
     after the last), pcs/ss the per-workgroup program counter and seq,
@@ -234,9 +244,13 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
     C = G - first if copiers is None else copiers
     if not 1 <= C <= G - first:
         raise ValueError(f"copiers {C} not in [1, {G - first}]")
-    if mutant == "M6" and C < 2:
-        raise ValueError("M6 needs at least two copying workgroups")
-    last_arrival = C - 2 if mutant == "M6" else C - 1
+    if poll_arrives and not poller:
+        raise ValueError("poll_arrives needs a poll workgroup")
+    NP = G + 1 if poll_arrives else G    # processes: the workgroups, and the poll workgroup's arrival wave
+    arrivals = C + 1 if poll_arrives else C
+    if mutant == "M6" and arrivals < 2:
+        raise ValueError("M6 needs at least two arrivals")
+    last_arrival = arrivals - 2 if mutant == "M6" else arrivals - 1
     nbuf = 1 if mutant == "M2" else 2
 
     def par_of(s):
@@ -244,9 +258,11 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
 
     def start_pc(g):
         # M8: a workgroup other than 0 counts itself finished before it reads the seq
-        return LASTOUT if (mutant == "M8" and g != 0) else READSEQ
+        return LASTOUT if (mutant == "M8" and 0 < g < G) else READSEQ
 
     def after_seq(g):
+        if g == G:                      # the poll workgroup's arrival wave
+            return ARRIVE
         if poller and g == 0:
             return LASTOUT if mutant == "M7" else WAIT
         if first <= g < first + C:
@@ -254,6 +270,8 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
         return LASTOUT if (early_finish and g != 0 and mutant != "M8") else WAIT
 
     def after_arrive(g):
+        if g == G:
+            return DONE
         if early_finish and (g != 0 or mutant == "M7") and not (mutant == "M8" and g != 0):
             return LASTOUT
         return WAIT
@@ -286,7 +304,7 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
 
     acts = [actions(r) for r in range(W)]
 
-    init_rank = (1, tuple(start_pc(g) for g in range(G)), (0,) * G, 0, 0, 0, 0, 0, 0,
+    init_rank = (1, tuple(start_pc(g) for g in range(NP)), (0,) * NP, 0, 0, 0, 0, 0, 0,
                  (0,) * (2 * G), (0,) * (2 * W * G), (0,) * W, 0, 0, 0)
     init = tuple(init_rank for _ in range(W))
 
@@ -305,7 +323,7 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
              send, recv, flag, posted, pcur, ppos) = st[r]
             # ---- GPU workgroups of rank r
             if c <= S:
-                for g in range(G):
+                for g in range(NP):
                     pc = pcs[g]
                     s = ss[g]
                     ns = None
@@ -364,6 +382,8 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                         ns = (c, pcs[:g] + (nxt,) + pcs[g + 1:], ss, cnt0, cnt1, go, seq_dev,
                               ctl_seq, done, send, recv, flag, posted, pcur, ppos)
                     elif pc == LASTOUT:
+                        if poll_arrives and g == 0 and pcs[G] != DONE and mutant != "M10":
+                            continue          # wait for the arrival wave
                         base = cnt0 if mutant == "M4" else cnt1
                         n1 = base + 1
                         sd, dn = seq_dev, done
@@ -382,7 +402,7 @@ def check_protocol(W: int, G: int, S: int, mutant: Optional[str] = None,
                                   ctl_seq, dn, send, recv, flag, posted, pcur, ppos)
                     if ns is not None and all(x == DONE for x in ns[1]):   # the kernel ends
                         c2 = c + 1
-                        pcs2 = tuple(start_pc(g2) if c2 <= S else FIN for g2 in range(G))
+                        pcs2 = tuple(start_pc(g2) if c2 <= S else FIN for g2 in range(NP))
                         final_cnt = (ns[3], ns[4])
                         if final_cnt != (0, 0):
                             return CheckResult(False, len(seen), (

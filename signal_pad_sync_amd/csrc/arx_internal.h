@@ -39,7 +39,7 @@ enum : uint64_t {
 // Device words (u32), each on its own 256-byte line of one allocation.
 enum : int {
   WORD_SEQ = 0,      // last completed seq (u64: words 0 and 1)
-  WORD_CNT0 = 64,    // workgroups past the copy (arrival counter)
+  WORD_CNT0 = 64,    // arrivals: copying workgroups past the copy, and the poll workgroup
   WORD_CNT1 = 128,   // workgroups finished (finish counter)
   WORD_GO = 192,     // go (u64): 2 * seq of the call whose peer data has all arrived, + 1 if that call
                      // is aborted; kGoReplicas copies, WORD_GO + 64 * k for replica k
@@ -66,7 +66,7 @@ struct OneShotArgs {
   uint32_t n;
   int rank;
   uint64_t timeout;        // wall-clock ticks per wait
-  uint32_t ncopy;          // workgroups that copy and count arrival (set by the launcher)
+  uint32_t ncopy;          // reducing workgroups that copy and count arrival (set by the launcher)
   uint32_t early_go;       // 1: go may precede this rank's publish (set by the launcher)
 };
 

@@ -32,6 +32,17 @@ namespace arx {
 // r < ncopy), counts arrival, waits for go and sums its share of vectors.
 // A grid of one workgroup does every step itself.
 //
+// The last of the arrivals (the copying workgroups' and the poll
+// workgroup's) publishes seq to the host proxy with a release store, tells
+// the poll workgroup so in the published word, and resets the arrival
+// counter (the next call's kernel starts after this one ends).
+__device__ __forceinline__ void publish_seq(const OneShotArgs& a, uint64_t seq, uint32_t* cnt0, uint64_t* published) {
+  fence_acquire_system();
+  store_release_system(&a.ctl->seq, seq);
+  store_relaxed_agent(published, seq);
+  store_relaxed_agent(cnt0, 0u);
+}
+
 // ONE_PASS: the G reducing workgroups have a thread for every 16-byte
 // vector. When every one of them copies (ncopy == G), each thread keeps
 // its own partial's vector in registers from the copy to the sum. Every
@@ -40,15 +51,31 @@ namespace arx {
 // G only when `in` and `out` do not overlap.
 template <int W, bool ONE_PASS, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
+  static_assert(BLOCK >= 128, "the poll workgroup uses two waves");
   __shared__ uint32_t s_abort;
+  __shared__ uint32_t s_arrived;
   uint64_t* const seq_dev = reinterpret_cast<uint64_t*>(a.words + WORD_SEQ);
   uint64_t* const published = reinterpret_cast<uint64_t*>(a.words + WORD_PUBLISHED);
   uint32_t* const cnt0 = a.words + WORD_CNT0;
   uint32_t* const cnt1 = a.words + WORD_CNT1;
   const bool single = gridDim.x == 1u;
 
-  // ---- the poll workgroup: its first wave only
+  // ---- the poll workgroup: two waves
   if (!single && blockIdx.x == 0) {
+    if (threadIdx.x == 0) s_arrived = 0u;
+    __syncthreads();
+    // The second wave stores this call's size for the proxy and counts one
+    // arrival, whose release carries that store; so the last arriver's
+    // release before the publish waits for no store to pinned memory (a
+    // PCIe write is acknowledged about 0.56 us after it is issued). It runs
+    // beside the first wave's flag wait; the first wave counts the
+    // workgroup finished only after it has arrived (below).
+    if (threadIdx.x == 64) {
+      const uint64_t s1 = load_relaxed_agent(seq_dev) + 1u;
+      store_relaxed_system(&a.ctl->bytes[(uint32_t)s1 & 1u], (uint64_t)a.n * 2u);
+      if (fetch_add_release_system(cnt0, 1u) == a.ncopy) publish_seq(a, s1, cnt0, published);
+      __hip_atomic_store(&s_arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if (threadIdx.x >= 64) return;
     const uint32_t lane = threadIdx.x;
     const bool peer = (int)lane < W && (int)lane != a.rank;
@@ -85,8 +112,17 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
     if (lane < kGoReplicas) store_relaxed_agent(go_word(a.words, lane), (seq << 1) | (bad ? 1u : 0u));
     if (lane == 0) {
       if (bad) report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
-      // the finish count, after the flag wait (see below); the last
-      // workgroup to count records the call as finished
+      // The finish count, after the flag wait (see below) and after the
+      // second wave's arrival: with a peer ahead, go and every other count
+      // can come before that wave has even read the seq, and a call
+      // recorded finished would let it read the next seq, arrive for that
+      // call and publish it before its copies. The wave has no wait of its
+      // own, so this one ends; the bound is only a guard.
+      const uint64_t t1 = now_ticks();
+      while (__hip_atomic_load(&s_arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u &&
+             now_ticks() - t1 <= a.timeout)
+        __builtin_amdgcn_s_sleep(1);
+      // the last workgroup to count records the call as finished
       if (fetch_add_relaxed_agent(cnt1, 1u) == gridDim.x - 1u) {
         store_relaxed_agent(cnt1, 0u);
         store_relaxed_agent(seq_dev, seq);
@@ -134,21 +170,15 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
 
   // 2. arrival count: one system-scope release per copying workgroup
   //    carries all its waves' copies (they precede it through the workgroup
-  //    barrier); the last to arrive acquires them all, resets the counter
-  //    and publishes seq to the host proxy, then tells the poll workgroup so
-  //    in the published word. A grid of one workgroup is its own last
-  //    arrival: its release store of seq carries the copies.
+  //    barrier); with the poll workgroup's arrival there are ncopy + 1, and
+  //    the last of them acquires them all and publishes (publish_seq). A
+  //    grid of one workgroup is its own last arrival: its release store of
+  //    seq carries the copies and the size.
   if (single && threadIdx.x == 0) {
     store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
     store_release_system(&a.ctl->seq, seq);
   } else if (copier && threadIdx.x == 0) {
-    if (fetch_add_release_system(cnt0, 1u) == a.ncopy - 1u) {
-      fence_acquire_system();
-      store_relaxed_agent(cnt0, 0u);
-      store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
-      store_release_system(&a.ctl->seq, seq);
-      store_relaxed_agent(published, seq);
-    }
+    if (fetch_add_release_system(cnt0, 1u) == a.ncopy) publish_seq(a, seq, cnt0, published);
   }
 
   // The finish count. It has to follow every workgroup's read of seq_dev

@@ -529,9 +529,11 @@ int arx_debug_set_seq(uint64_t seq) {
   for (int k = 0; k < arx::kGoReplicas; ++k)
     HIPCHK(hipMemcpy(S.words + arx::WORD_GO + 64 * k, &go, sizeof go, hipMemcpyHostToDevice));
   HIPCHK(hipMemcpy(S.words + arx::WORD_PUBLISHED, &seq, sizeof seq, hipMemcpyHostToDevice));
+  // The proxy first: were ctl.seq stored before its posted seq, the proxy
+  // thread could see the jump and post every seq up to it, one by one.
+  S.core->reset(seq);
   store_release(&S.ctl->done, seq);
   store_release(&S.ctl->seq, seq);
-  S.core->reset(seq);
   return ARX_OK;
 }
 

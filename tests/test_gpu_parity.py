@@ -397,8 +397,9 @@ def test_reduce_only_every_world(W):
 
 @pytest.mark.parametrize("mode", [arx.PROXY_LOCKSTEP, arx.PROXY_RUNAHEAD])
 def test_seq_crosses_32_bits(mode):
-    """Sequence numbers past 2^32: the device seq is 64-bit like the flags,
-    go's low 32 bits wrap, parity keeps alternating, every call bit-exact."""
+    """Sequence numbers past 2^32: the device seq, the go word (2 * seq +
+    abort) and the published word are 64-bit like the flags, parity keeps
+    alternating, every call bit-exact."""
     W, n, start = 4, 8192 + 3, (1 << 32) - 3
     recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
     xs = [WL.uniform(18000 + k, n) for k in range(8)]

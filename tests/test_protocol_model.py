@@ -89,44 +89,59 @@ def test_early_finish_mutants_are_caught():
 
 @pytest.mark.parametrize("W,G,S,C,early", [(2, 2, 3, None, False), (2, 3, 2, 1, False), (3, 2, 2, None, False),
                                            (2, 2, 3, None, True), (2, 3, 2, None, True), (2, 3, 2, 1, True),
-                                           (3, 2, 2, None, True)])
+                                           (3, 2, 1, None, True)])
 def test_protocol_with_poll_workgroup(W, G, S, C, early):
     """The kernel's grid of more than one workgroup: workgroup 0 only waits
     for the flags (possibly before any arrival, when a peer is ahead), gives
     go and counts itself finished; workgroups 1 .. G-1 hold the slices, the
-    first C of them copy. Safe, live, counters zero at every kernel end, and
-    the finished seq is recorded only after the flag wait."""
-    r = P.check_protocol(W, G, S, copiers=C, early_finish=early, poller=True)
-    assert r.ok, r.violation
-    assert r.finals == 1
-    # the same with go held back until this rank's own publish
-    r = P.check_protocol(W, G, S, copiers=C, early_finish=early, poller=True, go_after_publish=True)
-    assert r.ok, r.violation
-    assert r.finals == 1
+    first C of them copy. Checked as the kernel runs it, with the poll
+    workgroup's own arrival from a second wave (poll_arrives), with go held
+    back until this rank's publish as well (the rule past 4 vectors per
+    copying thread), and without that arrival. Safe, live, counters zero at
+    every kernel end, and the finished seq recorded only after the flag
+    wait."""
+    for kw in (dict(poll_arrives=True), dict(poll_arrives=True, go_after_publish=True), {}):
+        r = P.check_protocol(W, G, S, copiers=C, early_finish=early, poller=True, **kw)
+        assert r.ok, (kw, r.violation)
+        assert r.finals == 1, kw
 
 
 def test_poll_workgroup_mutants_are_caught():
-    """Every mutant still fails with a poll workgroup; M9 (go on this rank's
-    own publish, the published word, instead of the peers' flags) reduces
-    stale data, with or without a poll workgroup: the published word can
-    only say when to poll."""
-    for mutant in ["M1", "M2", "M3", "M4", "M5", "M9"]:
-        found = [P.check_protocol(W, G, S, mutant=mutant, poller=True) for W, G, S in [(2, 2, 3), (2, 3, 2)]]
-        assert all(not r.ok and r.violation for r in found), mutant
+    """Every mutant still fails with a poll workgroup and its arrival wave;
+    M9 (go on this rank's own publish, the published word, instead of the
+    peers' flags) reduces stale data, with or without a poll workgroup: the
+    published word can only say when to poll. M10 (the poll workgroup counts
+    itself finished before its arrival wave has arrived) lets that wave read
+    the next seq, arrive for the next call and publish it before its copies:
+    stale data."""
+    for kw in (dict(poll_arrives=True), {}):
+        for mutant in ["M1", "M2", "M3", "M4", "M5", "M9"]:
+            found = [P.check_protocol(W, G, S, mutant=mutant, poller=True, **kw) for W, G, S in [(2, 2, 3), (2, 3, 2)]]
+            assert all(not r.ok and r.violation for r in found), (mutant, kw)
+        for W, G, S, C in [(2, 3, 2, 2), (2, 3, 3, 2)]:
+            r = P.check_protocol(W, G, S, mutant="M6", copiers=C, poller=True, **kw)
+            assert not r.ok and "stale" in r.violation, (W, G, S, C, kw)
+        for W, G, S, C in [(2, 2, 3, None), (2, 3, 2, 1), (2, 3, 2, 2)]:
+            m7 = P.check_protocol(W, G, S, copiers=C, early_finish=True, mutant="M7", poller=True, **kw)
+            assert not m7.ok and "before workgroup 0 saw its flags" in m7.violation, (W, G, S, C, kw)
+            m8 = P.check_protocol(W, G, S, copiers=C, early_finish=True, mutant="M8", poller=True, **kw)
+            assert not m8.ok, (W, G, S, C, kw)
     for poller in (False, True):
         assert "stale" in P.check_protocol(2, 2, 3, mutant="M9", poller=poller).violation
-    for W, G, S, C in [(2, 3, 2, 2), (2, 3, 3, 2)]:
-        r = P.check_protocol(W, G, S, mutant="M6", copiers=C, poller=True)
-        assert not r.ok and "stale" in r.violation, (W, G, S, C)
-    for W, G, S, C in [(2, 2, 3, None), (2, 3, 2, 1), (2, 3, 2, 2)]:
-        m7 = P.check_protocol(W, G, S, copiers=C, early_finish=True, mutant="M7", poller=True)
-        assert not m7.ok and "before workgroup 0 saw its flags" in m7.violation, (W, G, S, C)
-        m8 = P.check_protocol(W, G, S, copiers=C, early_finish=True, mutant="M8", poller=True)
-        assert not m8.ok, (W, G, S, C)
+    # M6 with a single copier: the poll workgroup's arrival makes two
+    r = P.check_protocol(2, 2, 3, mutant="M6", poller=True, poll_arrives=True)
+    assert not r.ok and "stale" in r.violation
+    for W, G, S, C in [(2, 2, 3, None), (2, 3, 2, 1)]:
+        for early in (False, True):
+            m10 = P.check_protocol(W, G, S, copiers=C, early_finish=early, mutant="M10", poller=True,
+                                   poll_arrives=True)
+            assert not m10.ok and "stale" in m10.violation, (W, G, S, C, early)
     with pytest.raises(ValueError):
         P.check_protocol(2, 1, 2, poller=True)          # no reducing workgroup
     with pytest.raises(ValueError):
         P.check_protocol(2, 3, 2, copiers=3, poller=True)
+    with pytest.raises(ValueError):
+        P.check_protocol(2, 2, 2, poll_arrives=True)    # an arrival wave needs a poll workgroup
 
 
 @pytest.mark.parametrize("W,K", [(2, 1), (2, 3), (2, 4), (3, 2), (3, 3)])
