@@ -275,6 +275,35 @@ def test_in_place(mode, n):
             assert_bits(to_host(arx.send_view((k + 1) & 1, n)), xs[k], f"send slot of call {k + 1}")
 
 
+@pytest.mark.parametrize("mode", [arx.PROXY_LOCKSTEP, arx.PROXY_RUNAHEAD])
+def test_go_after_publish_past_4_vectors(mode):
+    """n = 8 Mi + 3 at W = 4 with in and out apart: 256 reducing workgroups
+    of 1024 threads, 128 of them copying, 8 vectors per copying thread, so
+    the poll workgroup holds go until this rank's publish even when the
+    peers' flags are already there (run-ahead). Every output is the
+    oracle's, the send slot holds each call's input, and every protocol
+    word is the model's."""
+    W, K, n = 4, 3, (1 << 23) + 3
+    recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
+    xs = [WL.own_partial(3, 11 + k, n) for k in range(K)]
+    pmode = P.RUNAHEAD if mode == arx.PROXY_RUNAHEAD else P.LOCKSTEP
+    with library(W, n + 5, mode=mode):
+        fill_recv(recv, 0)
+        st = None
+        out = sentinel(n + 5)
+        for k in range(K):
+            inp = to_dev(xs[k], pad_to=n + 5)
+            note(f"go after publish, n={n} mode={mode} call {k + 1}")
+            arx.allreduce(inp, out, n)
+            torch.cuda.synchronize()
+            st, outs = P.sequential_model([(xs[k], n)], recv, W, max_n=n + 5, state=st, mode=pmode)
+            got = to_host(out)
+            assert_bits(got[:n], outs[0], f"n={n}, call {k + 1}")
+            assert np.all(got[n:] == 0xDEAD)
+            assert_bits(to_host(arx.send_view((k + 1) & 1, n)), xs[k], f"send slot of call {k + 1}")
+        check_state(st, 0, wait_posted=st.posted)
+
+
 def test_manual_publish_and_order():
     """Manual mode: the kernel waits until the caller publishes; a publish
     out of order is refused and writes nothing."""
