@@ -45,11 +45,13 @@ enum : int {
                      // is aborted; kGoReplicas copies, WORD_GO + 64 * k for replica k
   WORD_PUBLISHED = 704,  // seq (u64) of the last call whose seq was published to the proxy: a hint
                          // that tells the flag wait when to read the peers' flags again
+  WORD_BYTES_SHADOW = 768,  // ctl.bytes[0] and ctl.bytes[1] as last stored (u64 at words 768 and 770)
   WORDS_TOTAL = 1024,
 };
 constexpr int kGoReplicas = 8;
 static_assert(WORD_GO + 64 * kGoReplicas <= WORD_PUBLISHED, "go replicas fit below the published word");
-static_assert(WORD_PUBLISHED + 64 <= WORDS_TOTAL, "the published word fits in the word block");
+static_assert(WORD_PUBLISHED + 64 <= WORD_BYTES_SHADOW, "the published word has a line of its own");
+static_assert(WORD_BYTES_SHADOW + 64 <= WORDS_TOTAL, "the size shadow fits in the word block");
 
 constexpr int kBlock = 256;       // threads per workgroup of the reduction kernels
 constexpr int kMaxOneShotGrid = 256;  // reducing workgroups of the one-shot kernel, at most

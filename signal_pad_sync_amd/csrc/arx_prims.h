@@ -68,6 +68,11 @@ __device__ __forceinline__ uint32_t fetch_add_release_system(uint32_t* p, uint32
   fence_release_system();
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+// The arrival counter takes system-scope atomics only (with or without a
+// release before them), so every arrival is performed at the same place.
+__device__ __forceinline__ uint32_t fetch_add_relaxed_system(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 __device__ __forceinline__ uint32_t fetch_add_relaxed_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -64,16 +64,32 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   if (!single && blockIdx.x == 0) {
     if (threadIdx.x == 0) s_arrived = 0u;
     __syncthreads();
-    // The second wave stores this call's size for the proxy and counts one
-    // arrival, whose release carries that store; so the last arriver's
-    // release before the publish waits for no store to pinned memory (a
-    // PCIe write is acknowledged about 0.56 us after it is issued). It runs
-    // beside the first wave's flag wait; the first wave counts the
-    // workgroup finished only after it has arrived (below).
+    // The second wave keeps this call's size for the proxy in
+    // ctl.bytes[par] and counts one arrival, so the last arriver's release
+    // before the publish waits for no store to pinned memory (a PCIe write
+    // is acknowledged about 0.56 us after it is issued). The size shadow
+    // holds both slots as last stored: when the slot already holds this
+    // size (the same n as two calls ago) nothing is stored, and the
+    // arrival, carrying nothing, is relaxed and comes well before the
+    // copiers'; otherwise the wave stores the size and its arrival's
+    // release carries it. It runs beside the first wave's flag wait; the
+    // first wave counts the workgroup finished only after it has arrived
+    // (below).
     if (threadIdx.x == 64) {
+      uint64_t* const shadow = reinterpret_cast<uint64_t*>(a.words + WORD_BYTES_SHADOW);
+      const uint64_t b0 = load_relaxed_agent(shadow), b1 = load_relaxed_agent(shadow + 1);
       const uint64_t s1 = load_relaxed_agent(seq_dev) + 1u;
-      store_relaxed_system(&a.ctl->bytes[(uint32_t)s1 & 1u], (uint64_t)a.n * 2u);
-      if (fetch_add_release_system(cnt0, 1u) == a.ncopy) publish_seq(a, s1, cnt0, published);
+      const uint32_t p1 = (uint32_t)s1 & 1u;
+      const uint64_t nb = (uint64_t)a.n * 2u;
+      uint32_t old;
+      if ((p1 ? b1 : b0) == nb) {
+        old = fetch_add_relaxed_system(cnt0, 1u);
+      } else {
+        store_relaxed_system(&a.ctl->bytes[p1], nb);
+        store_relaxed_agent(shadow + p1, nb);
+        old = fetch_add_release_system(cnt0, 1u);
+      }
+      if (old == a.ncopy) publish_seq(a, s1, cnt0, published);
       __hip_atomic_store(&s_arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     if (threadIdx.x >= 64) return;
@@ -176,6 +192,7 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   //    seq carries the copies and the size.
   if (single && threadIdx.x == 0) {
     store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
+    store_relaxed_agent(reinterpret_cast<uint64_t*>(a.words + WORD_BYTES_SHADOW) + par, (uint64_t)a.n * 2u);
     store_release_system(&a.ctl->seq, seq);
   } else if (copier && threadIdx.x == 0) {
     if (fetch_add_release_system(cnt0, 1u) == a.ncopy) publish_seq(a, seq, cnt0, published);

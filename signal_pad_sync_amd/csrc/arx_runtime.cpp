@@ -116,10 +116,14 @@ bool stress_copy(uint64_t s) {
   if (!S.stress_pool || !S.stress_stream) return false;
   const int par = (int)(s & 1);
   const uint16_t* set = S.stress_pool + (size_t)(s % (uint64_t)S.stress_sets) * S.world * S.max_n;
-  for (int src = 0; src < S.world; ++src) {
+  // As the page's proxy sends: the size the GPU published with seq s
+  // (ctl.bytes[s & 1], stored before the release of ctl.seq), not the slot.
+  const uint64_t bytes = load_acquire(&S.ctl->bytes[par]);
+  const size_t nb = bytes < S.max_n * sizeof(uint16_t) ? (size_t)bytes : S.max_n * sizeof(uint16_t);
+  for (int src = 0; src < S.world && nb > 0; ++src) {
     if (src == S.rank) continue;
-    if (hipMemcpyAsync(S.recv + ((size_t)par * S.world + src) * S.stride, set + (size_t)src * S.max_n,
-                       S.max_n * sizeof(uint16_t), hipMemcpyDeviceToDevice, S.stress_stream) != hipSuccess)
+    if (hipMemcpyAsync(S.recv + ((size_t)par * S.world + src) * S.stride, set + (size_t)src * S.max_n, nb,
+                       hipMemcpyDeviceToDevice, S.stress_stream) != hipSuccess)
       return false;
   }
   return hipStreamSynchronize(S.stress_stream) == hipSuccess;

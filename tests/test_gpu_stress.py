@@ -50,6 +50,43 @@ def test_fresh_peer_data_every_seq(W, n, sets, K):
             raise AssertionError(f"call {seq}: {bad.size} elements differ, first at {bad[0]}")
 
 
+@pytest.mark.parametrize("W", [4, 8])
+def test_call_size_changes(W):
+    """The proxy copies as many bytes as the GPU published with each seq
+    (ctl.bytes[seq & 1]), so a size left stale in its slot would leave the
+    tail of the peers' data from an older set and give a wrong sum. The
+    sizes repeat and change per parity: kept as they are, grown and shrunk,
+    with one workgroup (n <= 8192) and with several."""
+    ns = [9000, 9000, 20003, 20003, 9000, 50000, 50000, 50000, 20003, 9000, 9000, 4096, 4096, 60001, 9000]
+    sets, K, max_n = 5, len(ns), 60008
+    pool = np.stack([np.stack([WL.normal(8500 + 10 * k + src, max_n) for src in range(W)]) for k in range(sets)])
+    ins = [WL.normal(9500 + k + 1, n) for k, n in enumerate(ns)]
+    with library(W, max_n):
+        dpool = to_dev(pool.reshape(-1)).view(sets, W, max_n)
+        arx.set_stress_source(dpool, sets)
+        arx.set_proxy_mode(arx.PROXY_STRESS)
+        outs = []
+        for k, n in enumerate(ns):
+            note(f"stress W={W} call {k + 1}: n={n}")
+            out = torch.empty(max_n, dtype=torch.bfloat16, device="cuda")
+            arx.allreduce(to_dev(ins[k], pad_to=max_n), out, n)
+            outs.append(out)
+        torch.cuda.synchronize()
+        arx.set_proxy_mode(arx.PROXY_LOCKSTEP)
+        d = arx.debug_state()
+        assert d["ctl_err"] == 0 and d["seq_dev"] == K and d["posted"] == K, d
+        last = {p: 2 * ns[max(k for k in range(K) if (k + 1) % 2 == p)] for p in (0, 1)}
+        assert [d["ctl_bytes0"], d["ctl_bytes1"]] == [last[0], last[1]], d
+        got = [to_host(o) for o in outs]
+    for k, n in enumerate(ns):
+        seq = k + 1
+        parts = [ins[k]] + [pool[seq % sets][src][:n] for src in range(1, W)]
+        want = R.reduce(parts, n=n)
+        if not np.array_equal(got[k][:n], want):
+            bad = np.flatnonzero(got[k][:n] != want)
+            raise AssertionError(f"call {seq} (n={n}): {bad.size} elements differ, first at {bad[0]}")
+
+
 def test_stress_source_rules():
     with library(2, 64):
         with pytest.raises(arx.ArxError) as e:
