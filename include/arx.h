@@ -104,7 +104,8 @@ extern "C" {
  * [2][W][max_n] and symmetric buffers [W][max_n] bf16 in device memory, W
  * signal pads u32[ARX_MAX_PAD_BLOCKS][W], W x ARX_MAX_PAD_BLOCKS semaphores
  * and W x ARX_MAX_PAD_BLOCKS epochs, the device words (seq, two counters,
- * the go word in 8 replicas, the published seq), and in pinned coherent
+ * the go word in 8 replicas, the published seq, a copy of the two call
+ * sizes last stored), and in pinned coherent
  * host memory the control block and flags[W] (u64). Errors: ARX_EINVAL,
  * ARX_ESTATE (already initialised), ARX_ENOMEM, ARX_EHIP.
  */
