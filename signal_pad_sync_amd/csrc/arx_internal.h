@@ -153,4 +153,16 @@ unsigned oneshot_grid(uint32_t n, int block, unsigned max_grid);
 // Workgroups of a one-shot grid that copy the partial and count arrival.
 unsigned oneshot_copiers(unsigned grid);
 
+// Launch shape of one one-shot call with `block` threads per workgroup, at
+// most `resident` workgroups resident at once, and `in` and `out` apart or
+// not (the host-side rules of the launcher, also exported as a test aid).
+struct OneShotShape {
+  unsigned grid;      // reducing workgroups
+  unsigned launched;  // workgroups launched: grid, plus the poll workgroup when grid > 1
+  unsigned ncopy;     // reducing workgroups that copy and count arrival
+  bool one_pass;      // a reducing thread for every 16-byte vector
+  bool early_go;      // go may precede this rank's publish
+};
+OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoint);
+
 }  // namespace arx

@@ -342,6 +342,29 @@ static unsigned coresident(int cus) {
   return (unsigned)(cap < kMaxOneShotGrid + 1 ? cap : kMaxOneShotGrid + 1);
 }
 
+OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoint) {
+  OneShotShape sh{};
+  // the reducing workgroups; one more polls the flags when there are
+  // several, so all of them fit in resident - 1 (or make a grid of one)
+  sh.grid = oneshot_grid(n, block, resident > 1 ? resident - 1 : 1);
+  sh.launched = sh.grid > 1 ? sh.grid + 1 : 1;
+  sh.one_pass = (n >> 3) <= sh.grid * (uint32_t)block;
+  // With out == in, every reducing workgroup copies: each thread then
+  // copies a vector before it reduces (and overwrites) it. Were other
+  // workgroups copying, go could come before their copy (go follows the
+  // peers' flags, which a peer running ahead posts before this rank
+  // publishes) and the send slot would get the output instead of the input.
+  sh.ncopy = disjoint ? oneshot_copiers(sh.grid) : sh.grid;
+  // Go before the publish (a peer ahead) lets the workgroups that do not
+  // copy reduce while the copiers copy; past 4 vectors copied per copying
+  // thread the copiers then finish alone, and the call gets slower than
+  // with go after the publish (W=8, run-ahead peers, n = 16 Mi: 84.6 against
+  // 75.9 us; at n = 4 Mi, 2 vectors per reducing thread, early go is 1.8 us
+  // faster). So early go is allowed up to 4 vectors per copying thread.
+  sh.early_go = ((n >> 3) + sh.ncopy * block - 1) / (sh.ncopy * block) <= 4u;
+  return sh;
+}
+
 template <int W, int BLOCK>
 static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s) {
   // every workgroup waits on the others, so all must be resident together
@@ -349,31 +372,15 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   const unsigned cap1 = coresident<W, true, BLOCK>(cus);
   const unsigned resident = cap < cap1 ? cap : cap1;
   if (resident == 0) return hipErrorInvalidConfiguration;
-  // grid: the reducing workgroups; one more polls the flags when there are
-  // several, so all of them fit in resident - 1 (or make a grid of one)
-  const unsigned grid = oneshot_grid(a.n, BLOCK, resident > 1 ? resident - 1 : 1);
-  const bool one_pass = (a.n >> 3) <= grid * (uint32_t)BLOCK;
-  // With out == in, every reducing workgroup copies: each thread then
-  // copies a vector before it reduces (and overwrites) it. Were other
-  // workgroups copying, go could come before their copy (go follows the
-  // peers' flags, which a peer running ahead posts before this rank
-  // publishes) and the send slot would get the output instead of the input.
   const uint64_t ib = (uint64_t)(uintptr_t)a.in, ob = (uint64_t)(uintptr_t)a.out, nb = 2ull * a.n;
-  const bool disjoint = ib + nb <= ob || ob + nb <= ib;
+  const OneShotShape sh = oneshot_shape(a.n, BLOCK, resident, ib + nb <= ob || ob + nb <= ib);
   OneShotArgs b = a;
-  b.ncopy = disjoint ? oneshot_copiers(grid) : grid;
-  // Go before the publish (a peer ahead) lets the workgroups that do not
-  // copy reduce while the copiers copy; past 4 vectors copied per copying
-  // thread the copiers then finish alone, and the call gets slower than
-  // with go after the publish (W=8, run-ahead peers, n = 16 Mi: 84.6 against
-  // 75.9 us; at n = 4 Mi, 2 vectors per reducing thread, early go is 1.8 us
-  // faster). So early go is allowed up to 4 vectors per copying thread.
-  b.early_go = ((a.n >> 3) + b.ncopy * BLOCK - 1) / (b.ncopy * BLOCK) <= 4u ? 1u : 0u;
-  const unsigned launched = grid > 1 ? grid + 1 : 1;
-  if (one_pass)
-    hipLaunchKernelGGL((oneshot_kernel<W, true, BLOCK>), dim3(launched), dim3(BLOCK), 0, s, b);
+  b.ncopy = sh.ncopy;
+  b.early_go = sh.early_go ? 1u : 0u;
+  if (sh.one_pass)
+    hipLaunchKernelGGL((oneshot_kernel<W, true, BLOCK>), dim3(sh.launched), dim3(BLOCK), 0, s, b);
   else
-    hipLaunchKernelGGL((oneshot_kernel<W, false, BLOCK>), dim3(launched), dim3(BLOCK), 0, s, b);
+    hipLaunchKernelGGL((oneshot_kernel<W, false, BLOCK>), dim3(sh.launched), dim3(BLOCK), 0, s, b);
   return hipGetLastError();
 }
 

@@ -555,6 +555,23 @@ int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream)
   return ARX_OK;
 }
 
+int arx_test_oneshot_shape(size_t n, int block, unsigned resident, int in_place, int* out, int nout) {
+  if (n > ARX_MAX_N) return fail(ARX_EINVAL, "n %zu above ARX_MAX_N", n);
+  if (block != 0 && block != 256 && block != 512 && block != 1024) return fail(ARX_EINVAL, "block %d", block);
+  if (resident == 0) return fail(ARX_EINVAL, "no resident workgroup");
+  if (out == nullptr || nout < 6) return fail(ARX_EINVAL, "out needs 6 entries");
+  const int b = block ? block : arx::oneshot_block((uint32_t)n);
+  const unsigned cap = resident < arx::kMaxOneShotGrid + 1u ? resident : arx::kMaxOneShotGrid + 1u;
+  const arx::OneShotShape sh = arx::oneshot_shape((uint32_t)n, b, cap, in_place == 0);
+  out[0] = b;
+  out[1] = (int)sh.grid;
+  out[2] = (int)sh.launched;
+  out[3] = (int)sh.ncopy;
+  out[4] = sh.one_pass ? 1 : 0;
+  out[5] = sh.early_go ? 1 : 0;
+  return ARX_OK;
+}
+
 const char* arx_strerror(int err) {
   static char buf[640];
   const char* base;

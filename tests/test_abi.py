@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
         assert must in names
     assert len(names) >= 15
     aids = declared(HEADERS[1:])
-    assert aids == ["arx_debug_fail_proxy", "arx_debug_set_seq", "arx_debug_state", "arx_test_round_bf16"]
+    assert aids == ["arx_debug_fail_proxy", "arx_debug_set_seq", "arx_debug_state", "arx_test_oneshot_shape",
+                    "arx_test_round_bf16"]
     assert not set(aids) & set(names)
 
 
