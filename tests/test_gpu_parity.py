@@ -304,20 +304,26 @@ def test_go_after_publish_past_4_vectors(mode):
         check_state(st, 0, wait_posted=st.posted)
 
 
-def test_manual_publish_and_order():
+@pytest.mark.parametrize("n", [4096, 131072])
+def test_manual_publish_and_order(n):
     """Manual mode: the kernel waits until the caller publishes; a publish
-    out of order is refused and writes nothing."""
-    W, n = 4, 4096
+    out of order is refused and writes nothing. n = 4096 runs the grid of
+    one workgroup; at n = 131072 the poll workgroup has read the flags
+    once, seen this rank's publish and is polling again when the caller
+    publishes, 5 ms later."""
+    W = 4
     recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
     x = WL.own_partial(3, 9, n)
     with library(W, n, mode=arx.PROXY_MANUAL):
         fill_recv(recv, 0)
         inp, out = to_dev(x), sentinel(n)
-        note("manual publish")
+        note(f"manual publish n={n}")
         arx.allreduce(inp, out, n)
         with pytest.raises(arx.ArxError) as e:
             arx.publish(2)
         assert e.value.code == arx.EORDER
+        time.sleep(0.005)
+        assert arx.status()[0] == 1             # this rank has published seq 1
         arx.publish(1)
         torch.cuda.synchronize()
         st, outs = P.sequential_model([(x, n)], recv, W, mode=P.MANUAL,
