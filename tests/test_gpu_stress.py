@@ -105,19 +105,21 @@ def test_stress_source_rules():
         arx.set_stress_source(None, 0)
 
 
-def test_proxy_failure_is_latched():
+@pytest.mark.parametrize("n", [4096, 131072])
+def test_proxy_failure_is_latched(n):
     """Page "arx.cu": a failed proxy post latches an error, and the next
     all-reduce refuses to run. Forced from the host: the proxy's next
     peer-data copy reports failure; the call in flight never gets its flags
-    and ends through its 20 ms flag wait, writing nothing."""
-    W, n = 2, 4096
+    and ends through its 20 ms flag wait, writing nothing (one workgroup at
+    n = 4096, the poll workgroup's grid at n = 131072)."""
+    W = 2
     with library(W, n, timeout_us=20000):
         pool = torch.zeros(W * n, dtype=torch.bfloat16, device="cuda")
         arx.set_stress_source(pool, 1)
         arx.set_proxy_mode(arx.PROXY_STRESS)
         inp, out = to_dev(WL.normal(8800, n)), to_dev(np.full(n, 0xDEAD, np.uint16))
         arx.debug_fail_proxy()
-        note("proxy failure: one call whose flags never come")
+        note(f"proxy failure n={n}: one call whose flags never come")
         arx.allreduce(inp, out, n)
         torch.cuda.synchronize()
         assert np.all(to_host(out) == 0xDEAD)
