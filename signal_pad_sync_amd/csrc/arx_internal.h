@@ -158,7 +158,7 @@ unsigned oneshot_copiers(unsigned grid);
 // not (the host-side rules of the launcher, also exported as a test aid).
 struct OneShotShape {
   unsigned grid;      // reducing workgroups
-  unsigned launched;  // workgroups launched: grid, plus the poll workgroup when grid > 1
+  unsigned launched;  // workgroups launched: grid, plus the poll workgroup
   unsigned ncopy;     // reducing workgroups that copy and count arrival
   bool one_pass;      // a reducing thread for every 16-byte vector
   bool early_go;      // go may precede this rank's publish

@@ -22,15 +22,14 @@ namespace arx {
 
 // ---- one-shot kernel --------------------------------------------------------
 
-// A grid of more than one workgroup has a poll workgroup and G = gridDim.x - 1
-// reducing workgroups. The poll workgroup (blockIdx 0, dispatched first)
+// The grid is a poll workgroup and G = gridDim.x - 1 >= 1 reducing
+// workgroups. The poll workgroup (blockIdx 0, dispatched first)
 // only reads the peers' flags and releases go (page "arx.cu", protocol
 // comment: only one block reads the flags, the others learn of them from
 // device memory); it neither copies nor reduces, so its reads over PCIe hold
 // up no copy, and a peer that is already ahead is seen about one PCIe read
 // after the kernel starts. Reducing workgroup r = blockIdx.x - 1 copies (if
 // r < ncopy), counts arrival, waits for go and sums its share of vectors.
-// A grid of one workgroup does every step itself.
 //
 // The last of the arrivals (the copying workgroups' and the poll
 // workgroup's) publishes seq to the host proxy with a release store, tells
@@ -58,10 +57,9 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   uint64_t* const published = reinterpret_cast<uint64_t*>(a.words + WORD_PUBLISHED);
   uint32_t* const cnt0 = a.words + WORD_CNT0;
   uint32_t* const cnt1 = a.words + WORD_CNT1;
-  const bool single = gridDim.x == 1u;
 
   // ---- the poll workgroup: two waves
-  if (!single && blockIdx.x == 0) {
+  if (blockIdx.x == 0) {
     if (threadIdx.x == 0) s_arrived = 0u;
     __syncthreads();
     // The second wave keeps this call's size for the proxy in
@@ -148,9 +146,9 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
     return;
   }
 
-  // ---- the reducing workgroups (or the single one)
-  const uint32_t nred = single ? 1u : gridDim.x - 1u;
-  const uint32_t r = single ? 0u : blockIdx.x - 1u;
+  // ---- the reducing workgroups
+  const uint32_t nred = gridDim.x - 1u;
+  const uint32_t r = blockIdx.x - 1u;
   const uint32_t nv = a.n >> 3, tail = a.n & 7u;
   const uint32_t tid = r * BLOCK + threadIdx.x;
   const uint32_t nthr = nred * BLOCK;
@@ -187,14 +185,8 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // 2. arrival count: one system-scope release per copying workgroup
   //    carries all its waves' copies (they precede it through the workgroup
   //    barrier); with the poll workgroup's arrival there are ncopy + 1, and
-  //    the last of them acquires them all and publishes (publish_seq). A
-  //    grid of one workgroup is its own last arrival: its release store of
-  //    seq carries the copies and the size.
-  if (single && threadIdx.x == 0) {
-    store_relaxed_system(&a.ctl->bytes[par], (uint64_t)a.n * 2u);
-    store_relaxed_agent(reinterpret_cast<uint64_t*>(a.words + WORD_BYTES_SHADOW) + par, (uint64_t)a.n * 2u);
-    store_release_system(&a.ctl->seq, seq);
-  } else if (copier && threadIdx.x == 0) {
+  //    the last of them acquires them all and publishes (publish_seq)
+  if (copier && threadIdx.x == 0) {
     if (fetch_add_release_system(cnt0, 1u) == a.ncopy) publish_seq(a, seq, cnt0, published);
   }
 
@@ -208,57 +200,27 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   // reduction; moving the count took 0.8-1.0 us off a 256 KiB call on
   // MI355X.)
   uint32_t finished = 0;
-  if (!single && threadIdx.x == 0) finished = fetch_add_relaxed_agent(cnt1, 1u);
+  if (threadIdx.x == 0) finished = fetch_add_relaxed_agent(cnt1, 1u);
 
-  // 3. a grid of one workgroup waits for the flags itself (its first wave,
-  //    one lane per peer); the reducing workgroups of a larger grid wait for
-  //    go from the poll workgroup, then take an agent-scope acquire
-  bool abort;
-  if (single) {
-    if (threadIdx.x < 64) {
-      bool ok = true;
-      if ((int)threadIdx.x < W && (int)threadIdx.x != a.rank) {
-        const uint64_t t0 = now_ticks();
-        while (load_relaxed_system(a.flags + threadIdx.x) < seq) {
-          if (now_ticks() - t0 > a.timeout) {
-            ok = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
+  // 3. wait for go from the poll workgroup, then an agent-scope acquire
+  if (threadIdx.x == 0) {
+    const uint64_t* const go = go_word(a.words, blockIdx.x % kGoReplicas);
+    const uint64_t t0 = now_ticks();
+    bool timed = false;
+    uint64_t g;
+    while (((g = load_relaxed_agent(go)) >> 1) < seq) {
+      if (now_ticks() - t0 > 2u * a.timeout) {
+        timed = true;
+        break;
       }
-      const bool bad = __any(!ok);
-      fence_acquire_system();   // nobody to release to
-      if (threadIdx.x < kGoReplicas) store_relaxed_agent(go_word(a.words, threadIdx.x), (seq << 1) | (bad ? 1u : 0u));
-      if (threadIdx.x == 0) {
-        if (bad) report_error(a.ctl, ERR_FLAG_TIMEOUT, seq);
-        s_abort = bad ? 1u : 0u;
-      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    // the other waves are ordered after the first wave's acquire by the
-    // workgroup barrier
-    __syncthreads();
-    abort = s_abort != 0u;
-  } else {
-    if (threadIdx.x == 0) {
-      const uint64_t* const go = go_word(a.words, blockIdx.x % kGoReplicas);
-      const uint64_t t0 = now_ticks();
-      bool timed = false;
-      uint64_t g;
-      while (((g = load_relaxed_agent(go)) >> 1) < seq) {
-        if (now_ticks() - t0 > 2u * a.timeout) {
-          timed = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      fence_acquire_agent();
-      if (timed) report_error(a.ctl, ERR_GO_TIMEOUT, seq);
-      s_abort = (timed || (g & 1u) != 0u) ? 1u : 0u;
-    }
-    __syncthreads();
-    abort = s_abort != 0u;
+    fence_acquire_agent();
+    if (timed) report_error(a.ctl, ERR_GO_TIMEOUT, seq);
+    s_abort = (timed || (g & 1u) != 0u) ? 1u : 0u;
   }
+  __syncthreads();
+  const bool abort = s_abort != 0u;
 
   // 4. rank-ordered W-way sum; peer slots are read with system-coherent
   //    loads, since another agent wrote them
@@ -295,14 +257,13 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   }
 
   // 5. last block out: the last workgroup to count itself finished resets
-  //    the finish counter and records the completed seq (a grid of one
-  //    workgroup needs no count). Relaxed: the only reader of the counter
+  //    the finish counter and records the completed seq. Relaxed: the only reader of the counter
   //    and of seq_dev is the next kernel on the stream, which the kernel
   //    boundary orders after this one; ctl.done is progress information for
   //    the host's watchdog.
   if (threadIdx.x == 0) {
-    if (single || finished == gridDim.x - 1u) {
-      if (!single) store_relaxed_agent(cnt1, 0u);
+    if (finished == gridDim.x - 1u) {
+      store_relaxed_agent(cnt1, 0u);
       store_relaxed_agent(seq_dev, seq);
       store_relaxed_system(&a.ctl->done, seq);
     }
@@ -344,10 +305,10 @@ static unsigned coresident(int cus) {
 
 OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoint) {
   OneShotShape sh{};
-  // the reducing workgroups; one more polls the flags when there are
-  // several, so all of them fit in resident - 1 (or make a grid of one)
-  sh.grid = oneshot_grid(n, block, resident > 1 ? resident - 1 : 1);
-  sh.launched = sh.grid > 1 ? sh.grid + 1 : 1;
+  if (resident < 2) return sh;  // no room for the poll workgroup: grid 0
+  // the reducing workgroups, in resident - 1 beside the poll workgroup
+  sh.grid = oneshot_grid(n, block, resident - 1);
+  sh.launched = sh.grid + 1;
   sh.one_pass = (n >> 3) <= sh.grid * (uint32_t)block;
   // With out == in, every reducing workgroup copies: each thread then
   // copies a vector before it reduces (and overwrites) it. Were other
@@ -371,7 +332,7 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   const unsigned cap = coresident<W, false, BLOCK>(cus);
   const unsigned cap1 = coresident<W, true, BLOCK>(cus);
   const unsigned resident = cap < cap1 ? cap : cap1;
-  if (resident == 0) return hipErrorInvalidConfiguration;
+  if (resident < 2) return hipErrorInvalidConfiguration;
   const uint64_t ib = (uint64_t)(uintptr_t)a.in, ob = (uint64_t)(uintptr_t)a.out, nb = 2ull * a.n;
   const OneShotShape sh = oneshot_shape(a.n, BLOCK, resident, ib + nb <= ob || ob + nb <= ib);
   OneShotArgs b = a;
@@ -384,22 +345,20 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   return hipGetLastError();
 }
 
-// Threads per one-shot workgroup. Up to 1024 vectors: one workgroup of the
-// smallest size that holds them, so nothing waits on the go broadcast
-// (0.4-0.6 us faster than 2 or 4 workgroups at n = 4 Ki and 8 Ki for W
-// from 2 to 8; at W = 8, n = 8 Ki, a tie). Beyond: 256 while that keeps the
-// grid within 32 workgroups, 512 while within 64 (where half of them copy),
-// else 1024. Fewer workgroups mean fewer arrivals, go pollers and
-// last-block-out atomics, more threads per workgroup a longer copy and
-// reduction per workgroup. Measured on MI355X at W=8, lockstep, for n from
-// 16 Ki to 768 Ki elements; at n = 128 Ki, 512 threads (32 workgroups)
-// take 8.36-8.39 us per call, 256 threads (64 workgroups, 32 copying)
-// 8.63-8.67 us and 1024 threads 9.04-9.07 us.
+// Threads per one-shot workgroup: 256 while that keeps the reducing grid
+// within 32 workgroups, 512 while within 64 (where half of them copy), else
+// 1024. Fewer workgroups mean fewer arrivals, go pollers and last-block-out
+// atomics, more threads per workgroup a longer copy and reduction per
+// workgroup. Measured on MI355X at W=8, lockstep, for n from 16 Ki to
+// 768 Ki elements; at n = 128 Ki, 512 threads (32 workgroups) take
+// 8.36-8.39 us per call, 256 threads (64 workgroups, 32 copying)
+// 8.63-8.67 us and 1024 threads 9.04-9.07 us. Below 16 Ki elements 256
+// threads win as well: at n = 8 Ki, W=8, four workgroups of 256 take
+// 5.76-5.78 us (lockstep) and 4.22-4.24 us (peers ahead), two of 512
+// 5.90-6.01 and 4.32-4.35, one of 1024 6.37-6.40 and 4.83; at W=2 two of
+// 512 lead four of 256 by 0.1-0.2 us.
 int oneshot_block(uint32_t n) {
   const uint32_t nv = n >> 3;
-  if (nv <= 256u) return 256;
-  if (nv <= 512u) return 512;
-  if (nv <= 1024u) return 1024;
   if (nv <= 256u * 32u) return 256;
   if (nv <= 512u * 64u) return 512;
   return 1024;

@@ -304,13 +304,13 @@ def test_go_after_publish_past_4_vectors(mode):
         check_state(st, 0, wait_posted=st.posted)
 
 
-@pytest.mark.parametrize("n", [4096, 131072])
+@pytest.mark.parametrize("n", [1000, 131072])
 def test_manual_publish_and_order(n):
     """Manual mode: the kernel waits until the caller publishes; a publish
-    out of order is refused and writes nothing. n = 4096 runs the grid of
-    one workgroup; at n = 131072 the poll workgroup has read the flags
-    once, seen this rank's publish and is polling again when the caller
-    publishes, 5 ms later."""
+    out of order is refused and writes nothing. The poll workgroup has read
+    the flags once, seen this rank's publish and is polling again when the
+    caller publishes, 5 ms later; one reducing workgroup and a tail at
+    n = 1000, 32 at n = 131072."""
     W = 4
     recv = [WL.recv_partials(3, par, n, W) for par in (0, 1)]
     x = WL.own_partial(3, 9, n)
@@ -336,9 +336,10 @@ def test_manual_publish_and_order(n):
 def test_flag_timeout_is_latched(W, n):
     """No flag ever comes (manual mode, never published): the bounded wait
     runs out, the output stays untouched, counters still reset, seq advances,
-    and the next call reports the timeout. One workgroup (n = 4096), 32
-    workgroups all copying, and a grid-stride grid with half of them copying:
-    the others learn of the abort from the go word."""
+    and the next call reports the timeout. Two reducing workgroups
+    (n = 4096), 32 all copying, and a grid-stride grid with half of them
+    copying: the reducing workgroups learn of the abort from the go
+    word."""
     with library(W, n, mode=arx.PROXY_MANUAL, timeout_us=20000):
         inp, out = to_dev(np.ones(n, np.uint16)), sentinel(n)
         note(f"forced flag timeout (20 ms), W={W} n={n}")

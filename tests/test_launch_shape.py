@@ -1,20 +1,21 @@
 """The one-shot launch shape on the CPU (the library's host-side rules,
 through arx_test_oneshot_shape; no device is touched): the block size for
-n, one workgroup up to 1024 vectors, then 256 threads up to 32 reducing
-workgroups, 512 up to 64, else 1024; at most 256 reducing workgroups and,
-with more than one, the workgroup that waits for the flags besides; half of
-them copy from 64 on unless out == in; go may precede the publish only
-while a copying thread copies at most 4 vectors."""
+n, 256 threads up to 32 reducing workgroups, 512 up to 64, else 1024; at
+most 256 reducing workgroups (at least one) and the workgroup that waits
+for the flags besides; half of them copy from 64 on unless out == in; go
+may precede the publish only while a copying thread copies at most 4
+vectors."""
 import pytest
 
 from signal_pad_sync_amd import arx
 
 # (n, resident, in_place) -> block, reducing grid, launched, copiers, one pass, early go
 CASES = [
-    ((0, 257, False), (256, 1, 1, 1, 1, 1)),
-    ((8, 257, False), (256, 1, 1, 1, 1, 1)),
-    ((4096, 257, False), (512, 1, 1, 1, 1, 1)),
-    ((8192, 257, False), (1024, 1, 1, 1, 1, 1)),
+    ((0, 257, False), (256, 1, 2, 1, 1, 1)),
+    ((8, 257, False), (256, 1, 2, 1, 1, 1)),
+    ((1000, 257, False), (256, 1, 2, 1, 1, 1)),          # 125 vectors and a tail
+    ((4096, 257, False), (256, 2, 3, 2, 1, 1)),
+    ((8192, 257, False), (256, 4, 5, 4, 1, 1)),
     ((8200, 257, False), (256, 5, 6, 5, 1, 1)),          # 1025 vectors
     ((65536, 257, False), (256, 32, 33, 32, 1, 1)),
     ((65544, 257, False), (512, 17, 18, 17, 1, 1)),
@@ -27,7 +28,7 @@ CASES = [
     ((1 << 23, 257, True), (1024, 256, 257, 256, 0, 1)),          # in place, 4 per copying thread
     ((1 << 30, 257, False), (1024, 256, 257, 128, 0, 0)),
     ((131072, 32, False), (512, 31, 32, 31, 0, 1)),      # 32 resident (a partition of 32 CUs)
-    ((131072, 1, False), (512, 1, 1, 1, 0, 0)),          # room for one workgroup only
+    ((131072, 2, False), (512, 1, 2, 1, 0, 0)),          # room for the poll workgroup and one more
     ((131072, 100000, False), (512, 32, 33, 32, 1, 1)),  # resident capped at 257
 ]
 
@@ -45,7 +46,7 @@ def test_oneshot_shape_forced_block():
     assert arx.test_oneshot_shape(131072, 256)["ncopy"] == 32
 
 
-@pytest.mark.parametrize("n,block,resident", [((1 << 30) + 1, 0, 257), (64, 128, 257), (64, 0, 0)])
+@pytest.mark.parametrize("n,block,resident", [((1 << 30) + 1, 0, 257), (64, 128, 257), (64, 0, 0), (64, 0, 1)])
 def test_oneshot_shape_refuses(n, block, resident):
     with pytest.raises(arx.ArxError) as e:
         arx.test_oneshot_shape(n, block, resident)
