@@ -53,17 +53,19 @@ int arx_debug_fail_proxy(void);
  * pattern in[i]. in: device u32 [n], out: device u16 [n]; n <= 2^32 - 1. */
 int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream);
 
-/* The launch shape arx_allreduce uses for n elements (host-side rules
- * only; no device is touched): out[0] threads per workgroup (block = 0:
- * the library's choice for n, else 256, 512 or 1024), out[1] reducing
+/* The launch shape arx_allreduce uses for n elements at `world` partials
+ * (host-side rules only; no device is touched): out[0] threads per
+ * workgroup (block = 0: the library's choice for n and world, else 256,
+ * 512 or 1024), out[1] reducing
  * workgroups, out[2] workgroups launched (out[1], plus the workgroup that
  * waits for the flags), out[3] reducing workgroups that copy
  * the partial and count arrival, out[4] 1 if every vector has a thread of
  * its own, out[5] 1 if go may come before this rank's publish. resident:
  * workgroups the device holds at once (the library caps it at 257, the
  * most its grids use); in_place: out == in. Errors: ARX_EINVAL (n above
- * ARX_MAX_N, another block, resident below 2, out NULL or nout < 6). */
-int arx_test_oneshot_shape(size_t n, int block, unsigned resident, int in_place, int* out, int nout);
+ * ARX_MAX_N, world outside [2, 8], another block, resident below 2, out
+ * NULL or nout < 6). */
+int arx_test_oneshot_shape(size_t n, int world, int block, unsigned resident, int in_place, int* out, int nout);
 
 #ifdef __cplusplus
 }

@@ -55,7 +55,7 @@ SIGNATURES = [
     ("arx_debug_set_seq", _c.c_int, [_c.c_uint64]),
     ("arx_debug_fail_proxy", _c.c_int, []),
     ("arx_test_round_bf16", _c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
-    ("arx_test_oneshot_shape", _c.c_int, [_c.c_size_t, _c.c_int, _c.c_uint, _c.c_int,
+    ("arx_test_oneshot_shape", _c.c_int, [_c.c_size_t, _c.c_int, _c.c_int, _c.c_uint, _c.c_int,
                                           _c.POINTER(_c.c_int), _c.c_int]),
     ("arx_strerror", _c.c_char_p, [_c.c_int]),
     ("arx_max_n", _c.c_size_t, []),
@@ -276,9 +276,9 @@ def test_round_bf16(inp_u32, out_u16, stream=None):
                                    _stream(stream)))
 
 
-def test_oneshot_shape(n, block=0, resident=257, in_place=False) -> dict:
+def test_oneshot_shape(n, world=8, block=0, resident=257, in_place=False) -> dict:
     out = (_c.c_int * 6)()
-    _check(lib.arx_test_oneshot_shape(n, block, resident, 1 if in_place else 0, out, 6))
+    _check(lib.arx_test_oneshot_shape(n, world, block, resident, 1 if in_place else 0, out, 6))
     return dict(zip(("block", "grid", "launched", "ncopy", "one_pass", "early_go"), list(out)))
 
 

@@ -124,11 +124,11 @@ struct SymmArgs {
 };
 
 // Launchers (defined in arx_reduce.hip and arx_sync.hip). W in [2, 8]. block: threads per
-// one-shot workgroup (256, 512 or 1024), or 0 to choose by n. cus: compute
+// one-shot workgroup (256, 512 or 1024), or 0 to choose by n and W. cus: compute
 // units of the device; kernels whose workgroups wait on each other keep
 // their grid within what is resident at once.
 hipError_t launch_oneshot(const OneShotArgs& a, int W, int block, int cus, hipStream_t stream);
-int oneshot_block(uint32_t n);
+int oneshot_block(uint32_t n, int W);
 hipError_t launch_reduce(const ReduceArgs& a, int W, hipStream_t stream);
 // The barrier launchers: lanes = true puts block b of every rank in one wave
 // (nblocks workgroups), false gives rank v's block b a workgroup of its own

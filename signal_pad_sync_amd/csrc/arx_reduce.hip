@@ -346,27 +346,34 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
 }
 
 // Threads per one-shot workgroup: 256 while that keeps the reducing grid
-// within 32 workgroups, 512 while within 64 (where half of them copy), else
-// 1024. Fewer workgroups mean fewer arrivals, go pollers and last-block-out
-// atomics, more threads per workgroup a longer copy and reduction per
-// workgroup. Measured on MI355X at W=8, lockstep, for n from 16 Ki to
-// 768 Ki elements; at n = 128 Ki, 512 threads (32 workgroups) take
-// 8.36-8.39 us per call, 256 threads (64 workgroups, 32 copying)
-// 8.63-8.67 us and 1024 threads 9.04-9.07 us. Below 16 Ki elements 256
-// threads win as well: at n = 8 Ki, W=8, four workgroups of 256 take
-// 5.76-5.78 us (lockstep) and 4.22-4.24 us (peers ahead), two of 512
-// 5.90-6.01 and 4.32-4.35, one of 1024 6.37-6.40 and 4.83; at W=2 two of
-// 512 lead four of 256 by 0.1-0.2 us.
-int oneshot_block(uint32_t n) {
+// within 32 workgroups, 512 while within 64 (where half of them copy) for
+// W >= 5 and within 48 for W <= 4, else 1024. Fewer workgroups mean fewer
+// arrivals, go pollers and last-block-out atomics, more threads per
+// workgroup a longer copy and reduction per workgroup, and that reduction
+// is shorter the fewer partials it sums. Measured on MI355X, same box,
+// lockstep and with peers ahead:
+//  - W=8, n from 16 Ki to 768 Ki elements: at n = 128 Ki, 512 threads
+//    (32 workgroups) take 8.36-8.39 us per call, 256 threads (64, 32
+//    copying) 8.63-8.67 us and 1024 threads 9.04-9.07 us;
+//  - below 16 Ki elements 256 threads win too: at n = 8 Ki, W=8, four
+//    workgroups of 256 take 5.76-5.78 us (lockstep) and 4.22-4.24 us (peers
+//    ahead), two of 512 5.90-6.01 and 4.32-4.35, one of 1024 6.37-6.40 and
+//    4.83;
+//  - W from 2 to 7, n from 144 Ki to 256 Ki: past 48 workgroups of 512,
+//    32 of 1024 are 0.1-0.25 us faster at W <= 4 (W=2, n = 256 Ki:
+//    6.50-6.57 against 6.77-6.80 us lockstep, 4.77 against 4.94-4.95 with
+//    peers ahead) and slower or a tie at W >= 5 (W=7: 7.17-7.19 against
+//    7.11-7.12 and 5.53-5.54 against 5.27-5.28).
+int oneshot_block(uint32_t n, int W) {
   const uint32_t nv = n >> 3;
   if (nv <= 256u * 32u) return 256;
-  if (nv <= 512u * 64u) return 512;
+  if (nv <= 512u * (W <= 4 ? 48u : 64u)) return 512;
   return 1024;
 }
 
 template <int W>
 static hipError_t launch_oneshot_w(const OneShotArgs& a, int block, int cus, hipStream_t s) {
-  if (block == 0) block = oneshot_block(a.n);
+  if (block == 0) block = oneshot_block(a.n, W);
   switch (block) {
     case 256: return launch_oneshot_wb<W, 256>(a, cus, s);
     case 512: return launch_oneshot_wb<W, 512>(a, cus, s);

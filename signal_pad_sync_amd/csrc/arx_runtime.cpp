@@ -555,12 +555,13 @@ int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream)
   return ARX_OK;
 }
 
-int arx_test_oneshot_shape(size_t n, int block, unsigned resident, int in_place, int* out, int nout) {
+int arx_test_oneshot_shape(size_t n, int world, int block, unsigned resident, int in_place, int* out, int nout) {
   if (n > ARX_MAX_N) return fail(ARX_EINVAL, "n %zu above ARX_MAX_N", n);
+  if (world < 2 || world > 8) return fail(ARX_EINVAL, "world %d not in [2, 8]", world);
   if (block != 0 && block != 256 && block != 512 && block != 1024) return fail(ARX_EINVAL, "block %d", block);
   if (resident < 2) return fail(ARX_EINVAL, "resident %u: the poll workgroup and a reducing one need 2", resident);
   if (out == nullptr || nout < 6) return fail(ARX_EINVAL, "out needs 6 entries");
-  const int b = block ? block : arx::oneshot_block((uint32_t)n);
+  const int b = block ? block : arx::oneshot_block((uint32_t)n, world);
   const unsigned cap = resident < arx::kMaxOneShotGrid + 1u ? resident : arx::kMaxOneShotGrid + 1u;
   const arx::OneShotShape sh = arx::oneshot_shape((uint32_t)n, b, cap, in_place == 0);
   out[0] = b;

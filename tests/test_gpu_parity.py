@@ -275,6 +275,32 @@ def test_in_place(mode, n):
             assert_bits(to_host(arx.send_view((k + 1) & 1, n)), xs[k], f"send slot of call {k + 1}")
 
 
+@pytest.mark.parametrize("W,n", [(2, 196608), (2, 196616), (4, 262144), (5, 262144), (5, 196616)])
+def test_block_size_by_world(W, n):
+    """The block size depends on W past 48 workgroups of 512 threads: at
+    W <= 4, 1024 threads from n = 196616 on (25 to 32 workgroups, all
+    copying), at W >= 5 still 512 (49 to 64 workgroups, half copying from
+    64 on). Three calls each, rank 1, alternating parity, against the oracle,
+    with the send slot and every protocol word checked."""
+    K, rank = 3, 1
+    want_block = 1024 if (W <= 4 and (n >> 3) > 512 * 48) else 512
+    assert arx.test_oneshot_shape(n, W)["block"] == want_block
+    recv = [WL.recv_partials(4, par, n, W) for par in (0, 1)]
+    xs = [WL.own_partial(4, 21 + k, n) for k in range(K)]
+    with library(W, n, rank=rank):
+        fill_recv(recv, rank)
+        st = None
+        out = sentinel(n)
+        for k in range(K):
+            note(f"block by world, W={W} n={n} block={want_block} call {k + 1}")
+            arx.allreduce(to_dev(xs[k]), out, n)
+            torch.cuda.synchronize()
+            st, outs = P.sequential_model([(xs[k], n)], recv, W, rank=rank, max_n=n, state=st)
+            assert_bits(to_host(out), outs[0], f"W={W} n={n}, call {k + 1}")
+            assert_bits(to_host(arx.send_view((k + 1) & 1, n)), xs[k], f"send slot of call {k + 1}")
+        check_state(st, rank)
+
+
 @pytest.mark.parametrize("mode", [arx.PROXY_LOCKSTEP, arx.PROXY_RUNAHEAD])
 def test_go_after_publish_past_4_vectors(mode):
     """n = 8 Mi + 3 at W = 4 with in and out apart: 256 reducing workgroups

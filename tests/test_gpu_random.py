@@ -1,7 +1,7 @@
 """GPU: seeded random one-shot calls across the parameter space — W from 2
 to 8, this GPU at a random rank, lockstep or run-ahead proxy, n from 0 to
-max_n (up to 2 Mi elements, so every grid shape: one workgroup, several,
-the copy split and the grid-stride loop), in place or not, on uniformly
+max_n (up to 2 Mi elements, so every grid shape: one reducing workgroup,
+several, the copy split and the grid-stride loop), in place or not, on uniformly
 random bf16 bit patterns (Inf and NaN included). Every output is compared
 bit-exact with the oracle, the elements past n must keep their sentinel,
 and the send slot must hold the call's input."""

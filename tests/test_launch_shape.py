@@ -1,7 +1,7 @@
 """The one-shot launch shape on the CPU (the library's host-side rules,
 through arx_test_oneshot_shape; no device is touched): the block size for
-n, 256 threads up to 32 reducing workgroups, 512 up to 64, else 1024; at
-most 256 reducing workgroups (at least one) and the workgroup that waits
+n and the number of partials W, 256 threads up to 32 reducing workgroups,
+512 up to 64 (48 at W <= 4), else 1024; at most 256 reducing workgroups (at least one) and the workgroup that waits
 for the flags besides; half of them copy from 64 on unless out == in; go
 may precede the publish only while a copying thread copies at most 4
 vectors."""
@@ -9,7 +9,7 @@ import pytest
 
 from signal_pad_sync_amd import arx
 
-# (n, resident, in_place) -> block, reducing grid, launched, copiers, one pass, early go
+# (n, resident, in_place) at W = 8 -> block, reducing grid, launched, copiers, one pass, early go
 CASES = [
     ((0, 257, False), (256, 1, 2, 1, 1, 1)),
     ((8, 257, False), (256, 1, 2, 1, 1, 1)),
@@ -33,21 +33,45 @@ CASES = [
 ]
 
 
+# (n, W) -> the same; 512 threads end at 48 workgroups for W <= 4
+CASES_W = [
+    ((196608, 2), (512, 48, 49, 48, 1, 1)),
+    ((196616, 2), (1024, 25, 26, 25, 1, 1)),         # one vector past 48 x 512
+    ((196616, 4), (1024, 25, 26, 25, 1, 1)),
+    ((196616, 5), (512, 49, 50, 49, 1, 1)),
+    ((262144, 3), (1024, 32, 33, 32, 1, 1)),
+    ((262144, 5), (512, 64, 65, 32, 1, 1)),
+    ((131072, 2), (512, 32, 33, 32, 1, 1)),
+    ((8192, 2), (256, 4, 5, 4, 1, 1)),
+    ((1 << 20, 2), (1024, 128, 129, 64, 1, 1)),
+]
+
+FIELDS = ("block", "grid", "launched", "ncopy", "one_pass", "early_go")
+
+
 @pytest.mark.parametrize("args,want", CASES)
 def test_oneshot_shape(args, want):
     n, resident, in_place = args
-    got = arx.test_oneshot_shape(n, 0, resident, in_place)
-    assert tuple(got[k] for k in ("block", "grid", "launched", "ncopy", "one_pass", "early_go")) == want, got
+    got = arx.test_oneshot_shape(n, 8, 0, resident, in_place)
+    assert tuple(got[k] for k in FIELDS) == want, got
+
+
+@pytest.mark.parametrize("args,want", CASES_W)
+def test_oneshot_shape_by_world(args, want):
+    n, W = args
+    got = arx.test_oneshot_shape(n, W)
+    assert tuple(got[k] for k in FIELDS) == want, got
 
 
 def test_oneshot_shape_forced_block():
-    assert arx.test_oneshot_shape(131072, 1024)["grid"] == 16
-    assert arx.test_oneshot_shape(131072, 256)["grid"] == 64
-    assert arx.test_oneshot_shape(131072, 256)["ncopy"] == 32
+    assert arx.test_oneshot_shape(131072, 8, 1024)["grid"] == 16
+    assert arx.test_oneshot_shape(131072, 8, 256)["grid"] == 64
+    assert arx.test_oneshot_shape(131072, 8, 256)["ncopy"] == 32
 
 
-@pytest.mark.parametrize("n,block,resident", [((1 << 30) + 1, 0, 257), (64, 128, 257), (64, 0, 0), (64, 0, 1)])
-def test_oneshot_shape_refuses(n, block, resident):
+@pytest.mark.parametrize("n,W,block,resident", [((1 << 30) + 1, 8, 0, 257), (64, 8, 128, 257), (64, 8, 0, 0),
+                                                (64, 8, 0, 1), (64, 1, 0, 257), (64, 9, 0, 257)])
+def test_oneshot_shape_refuses(n, W, block, resident):
     with pytest.raises(arx.ArxError) as e:
-        arx.test_oneshot_shape(n, block, resident)
+        arx.test_oneshot_shape(n, W, block, resident)
     assert e.value.code == arx.EINVAL
