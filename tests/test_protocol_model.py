@@ -91,8 +91,9 @@ def test_early_finish_mutants_are_caught():
                                            (2, 2, 3, None, True), (2, 3, 2, None, True), (2, 3, 2, 1, True),
                                            (3, 2, 1, None, True)])
 def test_protocol_with_poll_workgroup(W, G, S, C, early):
-    """The kernel's grid of more than one workgroup: workgroup 0 only waits
-    for the flags (possibly before any arrival, when a peer is ahead), gives
+    """The kernel's grid, at every size (G = 2 is its smallest: the poll
+    workgroup and one reducing workgroup): workgroup 0 only waits for the
+    flags (possibly before any arrival, when a peer is ahead), gives
     go and counts itself finished; workgroups 1 .. G-1 hold the slices, the
     first C of them copy. Checked as the kernel runs it, with the poll
     workgroup's own arrival from a second wave (poll_arrives), with go held
