@@ -123,8 +123,9 @@ int arx_finalize(void);
 /*
  * arx_publish — the virtual peers publish seq: store-release flags[src] = seq
  * for every src != rank into pinned memory. seq must be exactly the last
- * posted seq + 1 (page "arx.cu": the proxy posts every seq in order, since a
- * skipped seq would let a peer accept a later flag over stale data);
+ * posted seq + 1 (page "arx.cu", proxy_loop: seqs are posted one by one with
+ * none left out, since a skipped seq would let a peer accept a later flag
+ * over stale data);
  * otherwise ARX_EORDER and nothing is written. Called by the proxy thread in
  * the lockstep and run-ahead modes, by the caller in manual mode.
  */

@@ -78,7 +78,7 @@ class ProtocolState:
     rank: int
     seq_dev: int = 0            # device u64: last completed seq
     cnt: List[int] = field(default_factory=lambda: [0, 0])  # arrival / finish counters
-    go: int = 0                 # device u32: low 32 bits of the seq whose peer data has all arrived
+    go: int = 0                 # device u32: low 32 bits of the seq whose peers' partials are all in place
     ctl_seq: int = 0            # pinned u64: last published seq
     ctl_bytes: List[int] = field(default_factory=lambda: [0, 0])  # bytes per parity
     ctl_done: int = 0           # pinned u64: last seq summed
@@ -93,8 +93,8 @@ class ProtocolState:
 
 def _post(st: ProtocolState, s: int) -> None:
     """The virtual peers publish seq s: every flag but this rank's becomes s.
-    Seqs are posted in order, none skipped (page "arx.cu", protocol comment
-    on the proxy posting every seq in order)."""
+    Seqs are posted in order, none skipped (page "arx.cu", the protocol
+    comment on the proxy)."""
     if s != st.posted + 1:
         raise ValueError(f"seq {s} posted out of order after {st.posted}")
     for src in range(st.W):

@@ -16,7 +16,7 @@ struct Semaphore;
 // line 2 is host-only.
 struct alignas(64) Ctl {
   uint64_t seq;       // last seq this GPU published
-  uint64_t bytes[2];  // bytes of the partial in send[parity]
+  uint64_t bytes[2];  // call size in bytes, one slot per parity of seq
   uint64_t pad0[5];
   uint64_t done;      // last seq whose reduction finished
   uint64_t err;       // first device-side error kind (ERR_*), 0 if none
@@ -41,7 +41,7 @@ enum : int {
   WORD_SEQ = 0,      // last completed seq (u64: words 0 and 1)
   WORD_CNT0 = 64,    // arrivals: copying workgroups past the copy, and the poll workgroup
   WORD_CNT1 = 128,   // workgroups finished (finish counter)
-  WORD_GO = 192,     // go (u64): 2 * seq of the call whose peer data has all arrived, + 1 if that call
+  WORD_GO = 192,     // go (u64): 2 * seq of the call whose peers' partials are all in place, + 1 if that call
                      // is aborted; kGoReplicas copies, WORD_GO + 64 * k for replica k
   WORD_PUBLISHED = 704,  // seq (u64) of the last call whose seq was published to the proxy: a hint
                          // that tells the flag wait when to read the peers' flags again

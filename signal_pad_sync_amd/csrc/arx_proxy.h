@@ -4,7 +4,7 @@
 // and against ordinary memory in host-only tests.
 //
 // Page "arx.cu", proxy_loop: the proxy watches the seq this rank published
-// and posts every seq in order, never skipping one (a skipped seq would let
+// and posts the seqs one after another, never skipping one (a skipped seq would let
 // a peer accept a later flag over stale data); between posts it is the
 // watchdog, which reports once when published work has not finished for
 // 2 s, with what this rank posted and each peer's flag.

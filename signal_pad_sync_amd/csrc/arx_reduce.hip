@@ -24,9 +24,9 @@ namespace arx {
 
 // The grid is a poll workgroup and G = gridDim.x - 1 >= 1 reducing
 // workgroups. The poll workgroup (blockIdx 0, dispatched first)
-// only reads the peers' flags and releases go (page "arx.cu", protocol
-// comment: only one block reads the flags, the others learn of them from
-// device memory); it neither copies nor reduces, so its reads over PCIe hold
+// only reads the peers' flags and releases go (page "arx.cu", arx_kernel:
+// flag polling is confined to one block, and go reaches the rest through a
+// device word); it neither copies nor reduces, so its reads over PCIe hold
 // up no copy, and a peer that is already ahead is seen about one PCIe read
 // after the kernel starts. Reducing workgroup r = blockIdx.x - 1 copies (if
 // r < ncopy), counts arrival, waits for go and sums its share of vectors.

@@ -5,7 +5,7 @@
 // Page "arx.cu": arx_prepare / arx_connect allocate and zero the pinned and
 // device state and start the proxy; arx_allreduce checks its arguments and
 // launches the kernel on the caller's stream; proxy_loop watches the
-// published seq, posts every seq in order and reports stalls.
+// published seq, posts the seqs one after another and reports stalls.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -88,8 +88,9 @@ int fail(int code, const char* fmt, ...) {
 inline uint64_t load_acquire(const uint64_t* p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
 inline void store_release(uint64_t* p, uint64_t v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
 
-// Proxy thread (page "arx.cu", proxy_loop): arx::Proxy posts every seq in
-// order up to the target the mode allows and runs the stall watchdog.
+// Proxy thread (page "arx.cu", proxy_loop): arx::Proxy posts seqs one by one,
+// none skipped, up to the target the mode allows, and runs the stall
+// watchdog.
 void proxy_main() {
   if (!S.core->run(S.stop)) {
     fprintf(stderr, "arx rank %d: proxy failed to post seq %llu\n", S.rank,

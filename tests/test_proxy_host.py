@@ -1,6 +1,6 @@
 """Host-only tests of the proxy thread and its stall watchdog (CPU only).
 
-The proxy class (page "arx.cu", proxy_loop: post every seq in order, report
+The proxy class (page "arx.cu", proxy_loop: post the seqs one after another, report
 stalls after 2 s) is built with g++ against a fake device thread in ordinary
 memory, once plainly, once under ThreadSanitizer and once under
 AddressSanitizer with UndefinedBehaviorSanitizer (host code only)."""
