@@ -199,7 +199,12 @@ long long barrier_groups_cap(bool counter, int cus) {
 // Copy and sum move kSymmU vectors per thread per pass with every load in
 // flight before the first use: 9.2 -> 8.0 us per iteration at W=8,
 // n = 128 Ki on MI355X, where one vector per pass paid a memory round trip
-// per vector (2 vectors per pass: 8.1 us).
+// per vector (2 vectors per pass: 8.1 us). The copy's and the sum's stores
+// write through the L2 (device scope) instead of staying dirty there, so
+// the release fence of pattern 1 finds nothing of theirs to write back:
+// 8.78-8.82 -> 7.49-7.58 us per iteration at W=8, n = 128 Ki (the copy's
+// stores alone: 7.56-7.66; nontemporal copy stores: 9.2), 4.16 -> 3.62 us
+// at W=2 and 5.32 -> 4.74 us at W=4.
 constexpr int kSymmU = 4;
 
 template <int W>
@@ -213,6 +218,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
 #pragma unroll
   for (int src = 0; src < W; ++src) rs[src] = make_rsrc(a.symm + (size_t)src * a.stride, slot_bytes(a.stride));
   const bool tail_block = b == a.blocks - 1;
+  const __amdgpu_buffer_rsrc_t rmine = make_rsrc(mine, slot_bytes(a.stride));
   // pattern 0
   bool ok = arx_detail::barrier_lane(a.pad, W, v, b, (int)threadIdx.x, false, a.timeout);
   if (__syncthreads_or(!ok)) goto fail;
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
 #pragma unroll
       for (int u = 0; u < kSymmU; ++u) {
         const uint32_t x = x0 + (uint32_t)u * kBlock;
-        if (x < hi) st16(mine + 8u * (size_t)x, t[u]);
+        if (x < hi) bstore16<CP_DEV>(rmine, x * 16u, t[u]);
       }
     }
     if (tail_block && threadIdx.x < tail) mine[8u * (size_t)nv + threadIdx.x] = in[8u * (size_t)nv + threadIdx.x];
@@ -239,6 +245,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
     __syncthreads();
     ok = arx_detail::barrier_lane(a.pad, W, v, b, (int)threadIdx.x, true, a.timeout);
     if (__syncthreads_or(!ok)) goto fail;
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out, a.n * 2u);
     for (uint32_t x0 = lo + threadIdx.x; x0 < hi; x0 += kSymmU * kBlock) {
       u32x4 y[kSymmU][W];
 #pragma unroll
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
 #pragma unroll
       for (int u = 0; u < kSymmU; ++u) {
         const uint32_t x = x0 + (uint32_t)u * kBlock;
-        if (x < hi) st16(out + 8u * (size_t)x, sum_bf16x8<W>(y[u]));
+        if (x < hi) bstore16<CP_DEV>(rout, x * 16u, sum_bf16x8<W>(y[u]));
       }
     }
     if (tail_block && threadIdx.x < tail) {
@@ -283,8 +290,12 @@ fail:
 // serialise per XCD, so fewer, fuller workgroups win until the per-thread
 // work dominates. Measured on MI355X for W = 2, 4 and 8 and n from 8 Ki to
 // 1 Mi elements, the rule is within a few percent of the best G at every
-// point; at W = 8, n = 128 Ki it takes 8.3 us per iteration where two
-// vectors per thread (32 per rank) took 10.6 us.
+// point; at W = 8, n = 128 Ki it took 8.3 us per iteration where two
+// vectors per thread (32 per rank) took 10.6 us. Swept again with the
+// write-through stores (targets of 64, 128 and 256 workgroups in all, W =
+// 2, 4, 8, n = 32 Ki to 512 Ki): 128 stays the best or within noise, the
+// others winning single points by at most 0.4 us (at W = 8, n = 128 Ki:
+// 7.38-7.46 us, against 9.6 for 64 and 8.3 for 256).
 template <int W>
 static int symm_blocks_w(uint32_t n, int cus) {
   static const int per_cu = [] {
