@@ -70,6 +70,7 @@ struct OneShotArgs {
   uint64_t timeout;        // wall-clock ticks per wait
   uint32_t ncopy;          // reducing workgroups that copy and count arrival (set by the launcher)
   uint32_t early_go;       // 1: go may precede this rank's publish (set by the launcher)
+  uint32_t nt_copy;        // 1: the copy's grid-stride stores are nontemporal (set by the launcher)
 };
 
 struct ReduceArgs {
@@ -162,6 +163,7 @@ struct OneShotShape {
   unsigned ncopy;     // reducing workgroups that copy and count arrival
   bool one_pass;      // a reducing thread for every 16-byte vector
   bool early_go;      // go may precede this rank's publish
+  bool nt_copy;       // the copy's grid-stride stores are nontemporal
 };
 OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoint);
 

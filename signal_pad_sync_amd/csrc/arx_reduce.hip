@@ -175,14 +175,21 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   //    the arrival has none of them left dirty to write back: at W=8 on
   //    MI355X, 6.45-6.49 -> 6.30-6.33 us per call at n = 128 Ki, 9.6 ->
   //    9.3 us at 1 Mi, 22.7 -> 20.8 us at 4 Mi and 76.4 -> 75.5 us at 16 Mi
-  //    (lockstep). Nontemporal stores were faster only at 16 Mi.
+  //    (lockstep). From 8 Mi elements on (nt_copy) they are nontemporal
+  //    instead, which leaves the last-level cache to the peers' partials:
+  //    36.3 -> 34.8 us at 8 Mi, 75.9 -> 74.4 us at 16 Mi and 157.9 ->
+  //    153.9 us at 32 Mi (below 8 Mi nontemporal stores lost on one box of
+  //    two). The grid then always loops, so only the loop has the choice.
   if (copier) {
     const __amdgpu_buffer_rsrc_t rmine = make_rsrc(mine, slot_bytes(a.stride));
     if (keep_own) {
       if (tid < nv) bstore16<CP_DEV>(rmine, tid * 16u, own);
     } else {
       const uint32_t cthr = a.ncopy * BLOCK;
-      for (uint32_t v = tid; v < nv; v += cthr) bstore16<CP_DEV>(rmine, v * 16u, ld16(a.in + 8u * (size_t)v));
+      if (a.nt_copy)
+        for (uint32_t v = tid; v < nv; v += cthr) bstore16<CP_NT>(rmine, v * 16u, ld16(a.in + 8u * (size_t)v));
+      else
+        for (uint32_t v = tid; v < nv; v += cthr) bstore16<CP_DEV>(rmine, v * 16u, ld16(a.in + 8u * (size_t)v));
     }
     if (tid < tail) mine[8u * (size_t)nv + tid] = a.in[8u * (size_t)nv + tid];
   }
@@ -329,6 +336,8 @@ OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoi
   // 75.9 us; at n = 4 Mi, 2 vectors per reducing thread, early go is 1.8 us
   // faster). So early go is allowed up to 4 vectors per copying thread.
   sh.early_go = ((n >> 3) + sh.ncopy * block - 1) / (sh.ncopy * block) <= 4u;
+  // nontemporal copy stores from 8 Mi elements on (see the kernel's copy)
+  sh.nt_copy = n >= (8u << 20);
   return sh;
 }
 
@@ -344,6 +353,7 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   OneShotArgs b = a;
   b.ncopy = sh.ncopy;
   b.early_go = sh.early_go ? 1u : 0u;
+  b.nt_copy = sh.nt_copy ? 1u : 0u;
   if (sh.one_pass)
     hipLaunchKernelGGL((oneshot_kernel<W, true, BLOCK>), dim3(sh.launched), dim3(BLOCK), 0, s, b);
   else

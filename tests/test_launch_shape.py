@@ -75,3 +75,15 @@ def test_oneshot_shape_refuses(n, W, block, resident):
     with pytest.raises(arx.ArxError) as e:
         arx.test_oneshot_shape(n, W, block, resident)
     assert e.value.code == arx.EINVAL
+
+
+@pytest.mark.parametrize("n,want", [(1 << 20, 0), ((8 << 20) - 1, 0), (8 << 20, 1), ((1 << 23) + 3, 1), (1 << 30, 1)])
+def test_oneshot_copy_stores_nontemporal_from_8_mi(n, want):
+    """From 8 Mi elements on the copy's stores are nontemporal, below they
+    write through; the grid loops there at every block size."""
+    for W in (2, 8):
+        for block in (0, 256, 1024):
+            got = arx.test_oneshot_shape(n, W, block)
+            assert got["nt_copy"] == want, (n, W, block, got)
+            if want:
+                assert got["one_pass"] == 0, got
