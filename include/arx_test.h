@@ -61,11 +61,12 @@ int arx_test_round_bf16(const void* in, void* out, size_t n, hipStream_t stream)
  * waits for the flags), out[3] reducing workgroups that copy
  * the partial and count arrival, out[4] 1 if every vector has a thread of
  * its own, out[5] 1 if go may come before this rank's publish, out[6] 1 if
- * the copy's stores are nontemporal (else write-through). resident:
+ * the copy's stores are nontemporal (else write-through), out[7] 1 if the
+ * sum's peer loads are nontemporal (else system-coherent). resident:
  * workgroups the device holds at once (the library caps it at 257, the
  * most its grids use); in_place: out == in. Errors: ARX_EINVAL (n above
  * ARX_MAX_N, world outside [2, 8], another block, resident below 2, out
- * NULL or nout < 7). */
+ * NULL or nout < 8). */
 int arx_test_oneshot_shape(size_t n, int world, int block, unsigned resident, int in_place, int* out, int nout);
 
 #ifdef __cplusplus

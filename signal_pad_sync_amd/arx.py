@@ -277,9 +277,9 @@ def test_round_bf16(inp_u32, out_u16, stream=None):
 
 
 def test_oneshot_shape(n, world=8, block=0, resident=257, in_place=False) -> dict:
-    out = (_c.c_int * 7)()
-    _check(lib.arx_test_oneshot_shape(n, world, block, resident, 1 if in_place else 0, out, 7))
-    return dict(zip(("block", "grid", "launched", "ncopy", "one_pass", "early_go", "nt_copy"), list(out)))
+    out = (_c.c_int * 8)()
+    _check(lib.arx_test_oneshot_shape(n, world, block, resident, 1 if in_place else 0, out, 8))
+    return dict(zip(("block", "grid", "launched", "ncopy", "one_pass", "early_go", "nt_copy", "nt_peer"), list(out)))
 
 
 class _DevArray:

@@ -71,6 +71,7 @@ struct OneShotArgs {
   uint32_t ncopy;          // reducing workgroups that copy and count arrival (set by the launcher)
   uint32_t early_go;       // 1: go may precede this rank's publish (set by the launcher)
   uint32_t nt_copy;        // 1: the copy's grid-stride stores are nontemporal (set by the launcher)
+  uint32_t nt_peer;        // 1: the grid-stride sum's peer loads are nontemporal (set by the launcher)
 };
 
 struct ReduceArgs {
@@ -164,7 +165,8 @@ struct OneShotShape {
   bool one_pass;      // a reducing thread for every 16-byte vector
   bool early_go;      // go may precede this rank's publish
   bool nt_copy;       // the copy's grid-stride stores are nontemporal
+  bool nt_peer;       // the grid-stride sum's peer loads are nontemporal
 };
-OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoint);
+OneShotShape oneshot_shape(uint32_t n, int W, int block, unsigned resident, bool disjoint);
 
 }  // namespace arx

@@ -175,11 +175,9 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
   //    the arrival has none of them left dirty to write back: at W=8 on
   //    MI355X, 6.45-6.49 -> 6.30-6.33 us per call at n = 128 Ki, 9.6 ->
   //    9.3 us at 1 Mi, 22.7 -> 20.8 us at 4 Mi and 76.4 -> 75.5 us at 16 Mi
-  //    (lockstep). From 8 Mi elements on (nt_copy) they are nontemporal
-  //    instead, which leaves the last-level cache to the peers' partials:
-  //    36.3 -> 34.8 us at 8 Mi, 75.9 -> 74.4 us at 16 Mi and 157.9 ->
-  //    153.9 us at 32 Mi (below 8 Mi nontemporal stores lost on one box of
-  //    two). The grid then always loops, so only the loop has the choice.
+  //    (lockstep). Once the peers' partials outgrow the last-level cache
+  //    (nt_copy, set by oneshot_shape) they are nontemporal instead; the
+  //    grid then always loops, so only the loop has the choice.
   if (copier) {
     const __amdgpu_buffer_rsrc_t rmine = make_rsrc(mine, slot_bytes(a.stride));
     if (keep_own) {
@@ -252,12 +250,25 @@ __global__ __launch_bounds__(BLOCK) void oneshot_kernel(OneShotArgs a) {
         st16(a.out + 8u * (size_t)tid, sum_bf16x8<W>(x));
       }
     } else {
-      for (uint32_t v = tid; v < nv; v += nthr) {
-        u32x4 x[W];
+      // Past the last-level cache (nt_peer, set by oneshot_shape) the peer
+      // loads stream nontemporally; after the acquire fence above they see
+      // the peers' data as the system-coherent ones do.
+      if (a.nt_peer) {
+        for (uint32_t v = tid; v < nv; v += nthr) {
+          u32x4 x[W];
 #pragma unroll
-        for (int src = 0; src < W; ++src)
-          x[src] = (src == a.rank) ? ld16(a.in + 8u * (size_t)v) : bload16<CP_SYS>(rs[src], v * 16u);
-        st16(a.out + 8u * (size_t)v, sum_bf16x8<W>(x));
+          for (int src = 0; src < W; ++src)
+            x[src] = (src == a.rank) ? ld16(a.in + 8u * (size_t)v) : bload16<CP_NT>(rs[src], v * 16u);
+          st16(a.out + 8u * (size_t)v, sum_bf16x8<W>(x));
+        }
+      } else {
+        for (uint32_t v = tid; v < nv; v += nthr) {
+          u32x4 x[W];
+#pragma unroll
+          for (int src = 0; src < W; ++src)
+            x[src] = (src == a.rank) ? ld16(a.in + 8u * (size_t)v) : bload16<CP_SYS>(rs[src], v * 16u);
+          st16(a.out + 8u * (size_t)v, sum_bf16x8<W>(x));
+        }
       }
     }
     if (tid < tail) {
@@ -316,7 +327,7 @@ static unsigned coresident(int cus) {
   return (unsigned)(cap < kMaxOneShotGrid + 1 ? cap : kMaxOneShotGrid + 1);
 }
 
-OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoint) {
+OneShotShape oneshot_shape(uint32_t n, int W, int block, unsigned resident, bool disjoint) {
   OneShotShape sh{};
   if (resident < 2) return sh;  // no room for the poll workgroup: grid 0
   // the reducing workgroups, in resident - 1 beside the poll workgroup
@@ -336,8 +347,21 @@ OneShotShape oneshot_shape(uint32_t n, int block, unsigned resident, bool disjoi
   // 75.9 us; at n = 4 Mi, 2 vectors per reducing thread, early go is 1.8 us
   // faster). So early go is allowed up to 4 vectors per copying thread.
   sh.early_go = ((n >> 3) + sh.ncopy * block - 1) / (sh.ncopy * block) <= 4u;
-  // nontemporal copy stores from 8 Mi elements on (see the kernel's copy)
-  sh.nt_copy = n >= (8u << 20);
+  // Cache policies once the peers' partials outgrow the 256 MiB last-level
+  // cache: both parities' peer slots take 4 n (W - 1) bytes. From 224 MiB
+  // (n (W - 1) >= 56 Mi) the copy's stores are nontemporal, from 384 MiB
+  // (96 Mi) the sum's peer loads too. Below, the peer data the benchmark
+  // re-reads every other call stays cached and the cached forms win.
+  // Measured on MI355X, lockstep, one box, write-through copy against
+  // nontemporal: W=8 36.7 -> 34.9 us at 8 Mi, 157 -> 153 at 32 Mi; W=4
+  // 83.5 -> 80.7 at 32 Mi but 43.0 -> 43.4 at 16 Mi and 23.4 -> 25.3 at
+  // 8 Mi; W=2 31.5 -> 33.8 at 16 Mi. Nontemporal peer loads on top: W=8
+  // 73.8 -> 69.5 at 16 Mi and 152.8 -> 127.5 at 32 Mi, but 34.9 -> 36.9 at
+  // 8 Mi; W=4 80.7 -> 76.7 at 32 Mi, 43.4 -> 44.5 at 16 Mi; W=2 57.3 ->
+  // 58.8 at 32 Mi.
+  const uint64_t peer = (uint64_t)n * (uint64_t)(W - 1);
+  sh.nt_copy = peer >= (56ull << 20);
+  sh.nt_peer = peer >= (96ull << 20);
   return sh;
 }
 
@@ -349,11 +373,12 @@ static hipError_t launch_oneshot_wb(const OneShotArgs& a, int cus, hipStream_t s
   const unsigned resident = cap < cap1 ? cap : cap1;
   if (resident < 2) return hipErrorInvalidConfiguration;
   const uint64_t ib = (uint64_t)(uintptr_t)a.in, ob = (uint64_t)(uintptr_t)a.out, nb = 2ull * a.n;
-  const OneShotShape sh = oneshot_shape(a.n, BLOCK, resident, ib + nb <= ob || ob + nb <= ib);
+  const OneShotShape sh = oneshot_shape(a.n, W, BLOCK, resident, ib + nb <= ob || ob + nb <= ib);
   OneShotArgs b = a;
   b.ncopy = sh.ncopy;
   b.early_go = sh.early_go ? 1u : 0u;
   b.nt_copy = sh.nt_copy ? 1u : 0u;
+  b.nt_peer = sh.nt_peer ? 1u : 0u;
   if (sh.one_pass)
     hipLaunchKernelGGL((oneshot_kernel<W, true, BLOCK>), dim3(sh.launched), dim3(BLOCK), 0, s, b);
   else

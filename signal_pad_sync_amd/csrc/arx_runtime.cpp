@@ -561,10 +561,10 @@ int arx_test_oneshot_shape(size_t n, int world, int block, unsigned resident, in
   if (world < 2 || world > 8) return fail(ARX_EINVAL, "world %d not in [2, 8]", world);
   if (block != 0 && block != 256 && block != 512 && block != 1024) return fail(ARX_EINVAL, "block %d", block);
   if (resident < 2) return fail(ARX_EINVAL, "resident %u: the poll workgroup and a reducing one need 2", resident);
-  if (out == nullptr || nout < 7) return fail(ARX_EINVAL, "out needs 7 entries");
+  if (out == nullptr || nout < 8) return fail(ARX_EINVAL, "out needs 8 entries");
   const int b = block ? block : arx::oneshot_block((uint32_t)n, world);
   const unsigned cap = resident < arx::kMaxOneShotGrid + 1u ? resident : arx::kMaxOneShotGrid + 1u;
-  const arx::OneShotShape sh = arx::oneshot_shape((uint32_t)n, b, cap, in_place == 0);
+  const arx::OneShotShape sh = arx::oneshot_shape((uint32_t)n, world, b, cap, in_place == 0);
   out[0] = b;
   out[1] = (int)sh.grid;
   out[2] = (int)sh.launched;
@@ -572,6 +572,7 @@ int arx_test_oneshot_shape(size_t n, int world, int block, unsigned resident, in
   out[4] = sh.one_pass ? 1 : 0;
   out[5] = sh.early_go ? 1 : 0;
   out[6] = sh.nt_copy ? 1 : 0;
+  out[7] = sh.nt_peer ? 1 : 0;
   return ARX_OK;
 }
 

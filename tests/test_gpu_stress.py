@@ -20,8 +20,15 @@ from tests.gpu_util import library, note, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("W,n,sets,K", [(8, 131072, 5, 200), (4, 262147, 3, 64), (2, 1000, 7, 100)])
+@pytest.mark.parametrize("W,n,sets,K", [(8, 131072, 5, 200), (4, 262147, 3, 64), (2, 1000, 7, 100),
+                                        (8, (8 << 20) + 3, 2, 4), (4, (32 << 20) + 5, 2, 4)])
 def test_fresh_peer_data_every_seq(W, n, sets, K):
+    """The proxy writes the peers' data for each seq just before its flag,
+    from a pool of `sets` data sets, so every call sums data no earlier call
+    saw. The two large cases run the copy's nontemporal stores (8 Mi + 3 at
+    W = 8) and the sum's nontemporal peer loads as well (32 Mi + 5 at
+    W = 4), which must see each seq's fresh data like the system-coherent
+    loads."""
     pool = np.stack([np.stack([WL.normal(8000 + 10 * k + src, n) for src in range(W)]) for k in range(sets)])
     npad = (n + 7) & ~7                               # rows start 16-byte aligned
     ins = np.zeros((K, npad), np.uint16)

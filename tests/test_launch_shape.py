@@ -77,13 +77,21 @@ def test_oneshot_shape_refuses(n, W, block, resident):
     assert e.value.code == arx.EINVAL
 
 
-@pytest.mark.parametrize("n,want", [(1 << 20, 0), ((8 << 20) - 1, 0), (8 << 20, 1), ((1 << 23) + 3, 1), (1 << 30, 1)])
-def test_oneshot_copy_stores_nontemporal_from_8_mi(n, want):
-    """From 8 Mi elements on the copy's stores are nontemporal, below they
-    write through; the grid loops there at every block size."""
-    for W in (2, 8):
-        for block in (0, 256, 1024):
-            got = arx.test_oneshot_shape(n, W, block)
-            assert got["nt_copy"] == want, (n, W, block, got)
-            if want:
-                assert got["one_pass"] == 0, got
+@pytest.mark.parametrize("n,W,copy,peer", [
+    (1 << 20, 8, 0, 0), ((8 << 20) - 1, 8, 0, 0), (8 << 20, 8, 1, 0), (12 << 20, 8, 1, 0),
+    (14 << 20, 8, 1, 1), (1 << 30, 8, 1, 1),
+    (16 << 20, 4, 0, 0), ((56 << 20) // 3 + 1, 4, 1, 0), (32 << 20, 4, 1, 1),
+    (32 << 20, 2, 0, 0), (56 << 20, 2, 1, 0), (96 << 20, 2, 1, 1)])
+def test_oneshot_cache_policies_past_the_last_level_cache(n, W, copy, peer):
+    """The copy's stores turn nontemporal once both parities' peer slots
+    take 224 MiB (n (W - 1) >= 56 Mi), the peer loads once they take
+    384 MiB (n (W - 1) >= 96 Mi); the grid loops there at every block
+    size, where the policies apply."""
+    want_copy = int(n * (W - 1) >= 56 << 20)
+    want_peer = int(n * (W - 1) >= 96 << 20)
+    assert (want_copy, want_peer) == (copy, peer)
+    for block in (0, 256, 1024):
+        got = arx.test_oneshot_shape(n, W, block)
+        assert (got["nt_copy"], got["nt_peer"]) == (want_copy, want_peer), (n, W, block, got)
+        if want_copy:
+            assert got["one_pass"] == 0, got
