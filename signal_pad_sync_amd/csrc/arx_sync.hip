@@ -204,7 +204,13 @@ long long barrier_groups_cap(bool counter, int cus) {
 // the release fence of pattern 1 finds nothing of theirs to write back:
 // 8.78-8.82 -> 7.49-7.58 us per iteration at W=8, n = 128 Ki (the copy's
 // stores alone: 7.56-7.66; nontemporal copy stores: 9.2), 4.16 -> 3.62 us
-// at W=2 and 5.32 -> 4.74 us at W=4.
+// at W=2 and 5.32 -> 4.74 us at W=4. From W = 6 on, the sum's stores are
+// nontemporal instead (the outputs are never read back here; the wider
+// sums stream more): at n = 128 Ki, W=6 8.65 -> 8.16-8.20 us, W=7
+// 9.45-9.49 -> 8.41-8.47, W=8 7.34-7.42 -> 7.05; at W = 5 and below they
+// tie or lose (W=5, n = 512 Ki: 10.6 -> 11.0 us).
+template <int W>
+constexpr int kSymmOutPolicy = W >= 6 ? CP_NT : CP_DEV;
 constexpr int kSymmU = 4;
 
 template <int W>
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(kBlock) void symm_allreduce_kernel(SymmArgs a) {
 #pragma unroll
       for (int u = 0; u < kSymmU; ++u) {
         const uint32_t x = x0 + (uint32_t)u * kBlock;
-        if (x < hi) bstore16<CP_DEV>(rout, x * 16u, sum_bf16x8<W>(y[u]));
+        if (x < hi) bstore16<kSymmOutPolicy<W>>(rout, x * 16u, sum_bf16x8<W>(y[u]));
       }
     }
     if (tail_block && threadIdx.x < tail) {
